@@ -1,0 +1,163 @@
+"""Seeded input recipes for paged MLA decode (no attention arithmetic here).
+
+Recipe (shared by every config):
+
+* RNG ``numpy.random.Generator(PCG64(seed))``; the five named workloads use
+  seed ``1000 + k`` for workload k.
+* Draw order: sequence lengths -> block permutation -> q -> kvcache ->
+  sparse index positions.
+* Values are float32 standard normals rounded once to bfloat16 (round to
+  nearest even, by torch's cast), drawn in chunks of 2**24 values.
+* Logical block j of request b lives in physical block ``block_table[b][j]``.
+  Physical blocks are a random permutation of the pool, handed out in batch
+  order; table entries past a request's last block are -1 (except the tiny
+  workload, whose table is the whole permutation reshaped).
+* Sparse indices are ``block * 64 + offset`` of sorted distinct positions,
+  with a tail of the sorted list replaced by -1.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+PAGE = 64
+CHUNK = 1 << 24
+
+
+def rng_for(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def bf16_from_f32(a: np.ndarray) -> torch.Tensor:
+    """Round float32 values to bfloat16 (RNE) as a CPU tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> torch.Tensor:
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.bfloat16)
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        out[s:e] = bf16_from_f32(rng.standard_normal(e - s, dtype=np.float32))
+    return out.view(*shape)
+
+
+def _table_from_perm(perm: np.ndarray, nblocks: np.ndarray, width: int) -> np.ndarray:
+    table = np.full((len(nblocks), width), -1, dtype=np.int32)
+    cur = 0
+    for b, n in enumerate(nblocks):
+        table[b, :n] = perm[cur:cur + n]
+        cur += n
+    return table
+
+
+def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
+                    seqlen_sampler=None, d_qk: int = 576, d_v: int = 512, h_kv: int = 1,
+                    causal: bool = False, spare_frac: float = 0.0, table_width=None,
+                    reshape_table: bool = False, name: str = "dense") -> dict:
+    """A dense paged-decode case.  ``seqlens`` fixed, or drawn by ``seqlen_sampler(rng)``."""
+    rng = rng_for(seed)
+    if seqlens is None:
+        seqlens = np.asarray(seqlen_sampler(rng), dtype=np.int64)
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    assert len(seqlens) == B
+    nblocks = (seqlens + PAGE - 1) // PAGE
+    n_used = int(nblocks.sum())
+    spare = int(math.ceil(spare_frac * n_used))
+    if reshape_table:
+        width = int(table_width)
+        pool = B * width
+        perm = rng.permutation(pool).astype(np.int32)
+        table = perm.reshape(B, width).copy()
+    else:
+        pool = max(1, n_used + spare)
+        width = int(table_width) if table_width is not None else max(1, int(nblocks.max(initial=0)))
+        perm = rng.permutation(pool).astype(np.int32)
+        table = _table_from_perm(perm, nblocks, width)
+    q = normal_bf16(rng, (B, s_q, h_q, d_qk))
+    kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
+    return dict(
+        name=name, sparse=False, q=q, kvcache=kv,
+        block_table=torch.from_numpy(table),
+        cache_seqlens=torch.from_numpy(seqlens.astype(np.int32)),
+        indices=None, s_q=s_q, h_q=h_q, h_kv=h_kv, d_qk=d_qk, d_v=d_v,
+        causal=bool(causal), softmax_scale=float(d_qk) ** -0.5,
+        active_h_q=h_q, topk=0,
+    )
+
+
+def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
+                     topk: int, cache_len: int, invalid_tail: int, d_qk: int = 512,
+                     d_v: int = 512, h_kv: int = 1, name: str = "sparse") -> dict:
+    """A top-k sparse-decode case: every request owns ``cache_len`` tokens of a
+    shared pool; each query token draws ``topk`` distinct positions, sorted,
+    and the last ``invalid_tail`` entries become -1."""
+    rng = rng_for(seed)
+    width = (cache_len + PAGE - 1) // PAGE
+    pool = B * width
+    perm = rng.permutation(pool).astype(np.int32)
+    table = perm.reshape(B, width)
+    q = normal_bf16(rng, (B, s_q, h_q, d_qk))
+    kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
+    idx = np.empty((B, s_q, topk), dtype=np.int32)
+    for b in range(B):
+        for i in range(s_q):
+            pos = np.sort(rng.choice(cache_len, size=topk, replace=False))
+            row = table[b, pos // PAGE].astype(np.int64) * PAGE + pos % PAGE
+            if invalid_tail:
+                row[topk - invalid_tail:] = -1
+            idx[b, i] = row
+    return dict(
+        name=name, sparse=True, q=q, kvcache=kv,
+        block_table=torch.from_numpy(table.copy()),
+        cache_seqlens=torch.full((B,), cache_len, dtype=torch.int32),
+        indices=torch.from_numpy(idx), s_q=s_q, h_q=h_q, h_kv=h_kv, d_qk=d_qk,
+        d_v=d_v, causal=False, softmax_scale=float(d_qk) ** -0.5,
+        active_h_q=active_h_q, topk=topk,
+    )
+
+
+def _c2_lens(rng):
+    return rng.integers(1, 4097, size=64)
+
+
+def _c4_lens(rng):
+    lo, hi = math.log(32768), math.log(131072)
+    long = np.floor(np.exp(rng.uniform(lo, hi, size=8))).astype(np.int64)
+    long = np.clip(long, 32768, 131072)
+    short = rng.integers(1, 257, size=8)
+    return np.concatenate([long, short])
+
+
+CONFIGS = {
+    1: dict(name="tiny: B=2 s_q=1 h_q=16 seqlens {64,200} pool 8",
+            kind="dense", B=2, s_q=1, h_q=16, seqlens=[64, 200], table_width=4,
+            reshape_table=True),
+    2: dict(name="varlen: B=64 s_q=1 h_q=128 seqlens U[1,4096] +10% spare blocks",
+            kind="dense", B=64, s_q=1, h_q=128, seqlen_sampler=_c2_lens, spare_frac=0.1,
+            table_width=64),
+    3: dict(name="MTP: B=128 s_q=2 causal h_q=128 seqlens 4096",
+            kind="dense", B=128, s_q=2, h_q=128, seqlens=[4096] * 128, causal=True,
+            table_width=64),
+    4: dict(name="skewed long context: B=16 s_q=1 h_q=64, 8 x logU[32k,128k] + 8 x U[1,256]",
+            kind="dense", B=16, s_q=1, h_q=64, seqlen_sampler=_c4_lens, table_width=2048),
+    5: dict(name="top-k sparse: B=32 s_q=1 h_q=64 (16 active) d_qk=d_v=512 topk 2048, 102 invalid",
+            kind="sparse", B=32, s_q=1, h_q=64, active_h_q=16, topk=2048, cache_len=65536,
+            invalid_tail=102, d_qk=512, d_v=512),
+}
+
+
+def make_config(k: int) -> dict:
+    """The five named workloads, seed 1000 + k."""
+    spec = dict(CONFIGS[k])
+    kind = spec.pop("kind")
+    name = spec.pop("name")
+    if kind == "dense":
+        return make_dense_case(1000 + k, name=name, **spec)
+    return make_sparse_case(1000 + k, name=name, **spec)
+
+
+def make_case(kind: str, seed: int, **kw) -> dict:
+    return make_dense_case(seed, **kw) if kind == "dense" else make_sparse_case(seed, **kw)
