@@ -1,0 +1,200 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) paged MLA decode library, libmla.so.
+ *
+ * Operation.  Multi-head latent attention decode over a paged latent cache, in
+ * "MQA mode": every cache token is one row of d_qk bf16 values (576 = 512 NoPE
+ * + 64 RoPE, or 512), the value is the first d_v = 512 columns of that same
+ * row, and all query heads share the single KV head (upstream FlashMLA README
+ * embedded in the DeepLink-org/flashmla-optimization page: "Support matrix" and
+ * its footnote on MQA mode; "FP8 KV Cache" for the row split).  Rows sit in
+ * 64-token pages reached through a block table (FlashMLA summary page on
+ * sourcepulse.org, "How It Works"; deepep.org usage page, "Block Table
+ * Manager").  The call sequence is the pages' one: metadata once per decode
+ * step from the sequence lengths and head configuration, then one decode call
+ * per layer that reuses it (deepep.org usage example; upstream README "Usage /
+ * MLA Decoding").  Sparse decode replaces the block table by per-query token
+ * indices (upstream README, "Sparse Attention (indices tensor)").
+ *
+ * For every request b, query token i < s_q and head h, with L = cache_seqlens[b]
+ * and n = L (or, when causal, min(L, max(0, L - s_q + i + 1))):
+ *     s_t  = softmax_scale * <q[b,i,h,:], K_t>              t < n
+ *     lse  = ln sum_t exp(s_t)                              (-inf when n == 0)
+ *     out  = sum_t exp(s_t - lse) * K_t[0:d_v]              (0 when n == 0)
+ * where K_t is cache row t of request b.  LSE is natural-log; the sparse-prefill
+ * equations of the upstream README use base 2 with log2(e)-scaled scores, which
+ * is the same value divided by ln 2.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are device memory owned by the caller; "host" is
+ *    host memory owned by the caller.  The library keeps no pointer after it
+ *    returns, allocates nothing, and holds no global state other than a
+ *    thread-local message for the last error.
+ *  - Tensors are dense and row-major (C-contiguous) in the layout stated.
+ *  - Decode calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  They neither synchronise nor allocate.
+ *  - Return value: MLA_OK (0), a positive warning, or a negative error code.
+ *    Errors are detected before any work is enqueued; nothing is written on
+ *    error.  mla_strerror() names a code, mla_last_error() gives details.
+ *  - Supported by the kernels: h_kv == 1, page_block_size == 64, d_qk in
+ *    {576, 512}, d_v == 512 (<= d_qk), bf16 q/kvcache/out.  Anything else
+ *    returns MLA_E_NOTSUP.
+ */
+#ifndef MLA_PAGED_KV_MLA_H
+#define MLA_PAGED_KV_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_OK = 0,
+  /* active_h_q was not in [1, h_q] or not a multiple of 8: all h_q heads are
+   * scheduled instead (the fail-closed rule of the DeepLink-org fork's
+   * runtime-switch section). */
+  MLA_W_ACTIVE_FALLBACK = 1,
+  MLA_E_INVAL = -1,  /* bad shape, stride, pointer or argument */
+  MLA_E_NOTSUP = -2, /* valid per the pages but not built here (h_kv != 1, ...) */
+  MLA_E_NOSPC = -3,  /* metadata array or workspace too small */
+  MLA_E_HIP = -4,    /* a HIP launch or query failed */
+};
+
+/* Metadata header; identical to the first 16 int32 of the metadata array. */
+typedef struct mla_sched_info {
+  int32_t num_parts;       /* parts holding >= 1 segment (workgroup columns) */
+  int32_t num_segments;    /* (unit, block range, slot) work items */
+  int32_t total_slots;     /* fp32 partial-result slots the workspace needs */
+  int32_t num_split_units; /* units cut into >= 2 segments (combine work) */
+  int32_t max_splits;      /* most segments of any one unit */
+  int32_t num_units;       /* dense: batch; sparse: batch * s_q */
+  int32_t quota;           /* per-part budget, in 64-token blocks */
+  int32_t total_cost;      /* sum over units of blocks + per-segment overhead */
+  int32_t target_parts;    /* part count the schedule was built for */
+  int32_t overhead;        /* per-segment overhead in blocks (5) */
+  int32_t row_blocks;      /* workgroups per part: ceil(rows / 64) */
+  int32_t rows;            /* query rows per unit: dense s_q*heads, sparse heads */
+  int32_t off_segs;        /* int offset of segs[num_segments][4] = (u, blk0, blk1, slot) */
+  int32_t off_num_splits;  /* int offset of num_splits[num_units + 1] (cumulative) */
+  int32_t off_split_list;  /* int offset of split_list[num_split_units][2] = (u, slot0) */
+  int32_t total_ints;      /* metadata length in int32 */
+} mla_sched_info;
+
+/* Library version, e.g. 0x00010000 for 1.0.0. */
+int32_t mla_version(void);
+
+/* Short name of a return code (static string). */
+const char* mla_strerror(int code);
+
+/* Details of the last non-OK return on the calling thread (static per thread). */
+const char* mla_last_error(void);
+
+/* Default part count for `rows` query rows per unit on a device with `num_cus`
+ * compute units: max(1, (2 * num_cus) / ceil(rows / 64)). */
+int32_t mla_default_num_parts(int32_t rows, int32_t num_cus);
+
+/* Upper bound, in int32, of the metadata for `num_units` units and at most
+ * `target_parts` parts: 18 + 5 * target_parts + 7 * num_units. */
+size_t mla_metadata_capacity(int32_t num_units, int32_t target_parts);
+
+/*
+ * mla_get_metadata -- tile scheduler (the pages' get_mla_metadata: deepep.org
+ * usage example; upstream README "Usage / MLA Decoding", six-argument form
+ * with h_q and topk).  Host only: no HIP call, no device memory.
+ *
+ *   cache_seqlens_host [batch] int32, host.  Dense mode only (topk == 0);
+ *                      may be NULL in sparse mode.  Values must be >= 0.
+ *   batch, s_q, h_q, h_kv   shapes of the decode call this metadata serves.
+ *   topk               0 = dense paged decode; > 0 = sparse decode with topk
+ *                      indices per query token (units are query tokens).
+ *   active_h_q         heads actually computed (the first active_h_q); 0 = h_q.
+ *                      Must be in [1, h_q] and a multiple of 8 (or equal to
+ *                      h_q); otherwise h_q is used and MLA_W_ACTIVE_FALLBACK is
+ *                      returned (DeepLink-org fork, runtime-switch section).
+ *   num_cus            compute units of the target device (used when
+ *                      num_parts == 0).
+ *   num_parts          target part count; 0 = mla_default_num_parts(rows, num_cus).
+ *   meta_host          [meta_capacity_ints] int32, host: receives the metadata
+ *                      array (header, part_ptr, segs, num_splits, split_list).
+ *                      The caller copies info->total_ints of it to the device
+ *                      for the decode calls.
+ *   info               receives the header.
+ *
+ * Schedule: units of nb = ceil(len / 64) blocks; total = sum(nb + 5);
+ * quota = ceil(total / P) + 5; parts are filled greedily in unit order, a unit
+ * is cut only when more than the 5-block overhead of budget is left, and a cut
+ * unit's segments get consecutive workspace slots.  At most P parts are used.
+ * Errors: MLA_E_INVAL (negative/zero shapes, h_q % h_kv, negative length,
+ * num_cus and num_parts both 0), MLA_E_NOSPC (meta_capacity_ints too small).
+ */
+int mla_get_metadata(const int32_t* cache_seqlens_host, int32_t batch, int32_t s_q,
+                     int32_t h_q, int32_t h_kv, int32_t topk, int32_t active_h_q,
+                     int32_t num_cus, int32_t num_parts, int32_t* meta_host,
+                     size_t meta_capacity_ints, mla_sched_info* info);
+
+/* Workspace bytes a decode call with this metadata needs (0 if nothing is
+ * split): fp32 partial outputs [total_slots, rows, d_v] then, 256-byte
+ * aligned, fp32 partial log-sum-exps [total_slots, rows]. */
+size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v);
+
+/*
+ * mla_decode_paged -- dense paged MLA decode (the pages' flash_mla_with_kvcache
+ * without indices: deepep.org usage example; upstream README "Usage / MLA
+ * Decoding").
+ *
+ *   q              [batch, s_q, h_q, d_qk] bf16, device.
+ *   kvcache        [num_blocks, page_block_size, h_kv, d_qk] bf16, device.
+ *   block_table    [batch, bt_stride] int32, device.  Entries for logical
+ *                  blocks below ceil(cache_seqlens[b] / 64) must be in
+ *                  [0, num_blocks); other entries are never read.
+ *   cache_seqlens  [batch] int32, device; the same values the metadata was
+ *                  built from.  Must be <= bt_stride * 64.
+ *   dv             value width (first dv columns of each cache row).
+ *   causal         0/1; bottom-right aligned (query i sees positions
+ *                  <= L - s_q + i).
+ *   softmax_scale  multiplies q.k (commonly d_qk^-0.5).
+ *   meta_dev, info metadata (device copy) and header from mla_get_metadata
+ *                  in dense mode with the same batch, s_q, h_q.
+ *   workspace      device, >= mla_workspace_bytes(info, dv) bytes (may be
+ *                  NULL when that is 0).
+ *   out            [batch, s_q, h_q, dv] bf16, device.
+ *   lse            [batch, s_q, h_q] fp32, device.
+ * Heads >= the metadata's active head count are not written.
+ */
+int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_table,
+                     const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                     int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                     int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                     float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
+                     void* workspace, size_t workspace_bytes, void* out, float* lse,
+                     void* stream);
+
+/*
+ * mla_decode_sparse -- token-level top-k sparse MLA decode (upstream README,
+ * "Sparse Attention (indices tensor)"; the DeepLink-org fork's active-head
+ * split/combine kernels).
+ *
+ *   q              [batch, s_q, h_q, d_qk] bf16, device.
+ *   kvcache        [num_blocks, page_block_size, h_kv, d_qk] bf16, device,
+ *                  addressed as [num_blocks * page_block_size, h_kv, d_qk].
+ *   indices        [batch, s_q, topk] int32, device: block * 64 + offset.  An
+ *                  entry < 0 or >= num_blocks * 64 is invalid and skipped; no
+ *                  block table is needed.
+ *   meta_dev, info from mla_get_metadata in sparse mode (topk > 0) with the
+ *                  same batch, s_q, h_q, topk; its active head count decides
+ *                  which heads are computed (the first ones).
+ *   out, lse       as for mla_decode_paged; heads >= active are not written.
+ */
+int mla_decode_sparse(const void* q, const void* kvcache, const int32_t* indices,
+                      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                      int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                      float softmax_scale, const int32_t* meta_dev,
+                      const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                      void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_KV_MLA_H */

@@ -1,0 +1,297 @@
+"""ctypes marshalling for libmla.so (argument checks, allocation, pointers)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import warnings
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_OK = 0
+MLA_W_ACTIVE_FALLBACK = 1
+
+_HEADER_FIELDS = [
+    "num_parts", "num_segments", "total_slots", "num_split_units", "max_splits", "num_units",
+    "quota", "total_cost", "target_parts", "overhead", "row_blocks", "rows", "off_segs",
+    "off_num_splits", "off_split_list", "total_ints",
+]
+
+
+class MlaSchedInfo(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in _HEADER_FIELDS]
+
+
+class MLAError(RuntimeError):
+    """A negative return code from libmla.so."""
+
+    def __init__(self, code: int, what: str, detail: str):
+        super().__init__(f"{what}: {detail} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m mla_paged_kv_amd.build). There is no fallback path.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    pinfo = ctypes.POINTER(MlaSchedInfo)
+    lib.mla_version.restype = i32
+    lib.mla_strerror.restype = ctypes.c_char_p
+    lib.mla_strerror.argtypes = [ctypes.c_int]
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_default_num_parts.restype = i32
+    lib.mla_default_num_parts.argtypes = [i32, i32]
+    lib.mla_metadata_capacity.restype = sz
+    lib.mla_metadata_capacity.argtypes = [i32, i32]
+    lib.mla_get_metadata.restype = ctypes.c_int
+    lib.mla_get_metadata.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, pinfo]
+    lib.mla_workspace_bytes.restype = sz
+    lib.mla_workspace_bytes.argtypes = [pinfo, i32]
+    lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                     i32, ctypes.c_float, vp, pinfo, vp, sz, vp, vp, vp]
+    lib.mla_decode_sparse.restype = ctypes.c_int
+    lib.mla_decode_sparse.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      ctypes.c_float, vp, pinfo, vp, sz, vp, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str) -> int:
+    if rc < 0:
+        lib = _load()
+        raise MLAError(rc, what, f"{lib.mla_strerror(rc).decode()}: {lib.mla_last_error().decode()}")
+    return rc
+
+
+class Metadata:
+    """Tile-scheduler output: host header + arrays, and the device copy."""
+
+    def __init__(self, info: MlaSchedInfo, meta_host: np.ndarray, meta_dev, *, sparse: bool,
+                 batch: int, s_q: int, h_q: int, topk: int):
+        self.info = info
+        self.meta_host = meta_host
+        self.meta_dev = meta_dev
+        self.sparse = sparse
+        self.batch, self.s_q, self.h_q, self.topk = batch, s_q, h_q, topk
+
+    def __getattr__(self, name):
+        if name in _HEADER_FIELDS:
+            return getattr(self.info, name)
+        raise AttributeError(name)
+
+    @property
+    def heads(self) -> int:
+        return self.info.rows if self.sparse else self.info.rows // self.s_q
+
+    @property
+    def num_splits(self) -> np.ndarray:
+        """Cumulative segment count per unit, [num_units + 1]."""
+        o = self.info.off_num_splits
+        return self.meta_host[o:o + self.info.num_units + 1]
+
+    @property
+    def segments(self) -> np.ndarray:
+        o = self.info.off_segs
+        return self.meta_host[o:o + 4 * self.info.num_segments].reshape(-1, 4)
+
+    def workspace_bytes(self, dv: int = 512) -> int:
+        return int(_load().mla_workspace_bytes(ctypes.byref(self.info), dv))
+
+
+def _num_cus(device) -> int:
+    return int(torch.cuda.get_device_properties(device).multi_processor_count)
+
+
+def mla_get_metadata(cache_seqlens, s_q: int, h_q: int, h_kv: int = 1, topk: int = 0,
+                     active_h_q: int = 0, num_parts: int = 0, num_cus: int | None = None,
+                     device=None, upload: bool = True) -> Metadata:
+    """Tile scheduler.  ``cache_seqlens``: [batch] ints (host or device; a device
+    tensor is copied to the host, which synchronises).  ``topk > 0`` selects
+    sparse mode.  Returns a :class:`Metadata` whose ``meta_dev`` lives on
+    ``device`` (default: the current CUDA device) unless ``upload`` is False."""
+    lib = _load()
+    if isinstance(cache_seqlens, torch.Tensor):
+        if device is None and cache_seqlens.is_cuda:
+            device = cache_seqlens.device
+        sl = cache_seqlens.detach().to("cpu", torch.int32).contiguous().numpy()
+    else:
+        sl = np.ascontiguousarray(np.asarray(cache_seqlens, dtype=np.int32))
+    batch = int(sl.shape[0])
+    if upload and device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    if num_cus is None:
+        num_cus = _num_cus(device) if (num_parts == 0) else 0
+    units = batch * s_q if topk > 0 else batch
+    if num_parts > 0:
+        target = num_parts
+    else:
+        # size for the requested head count and for the all-heads fallback
+        per_unit = s_q if topk == 0 else 1
+        target = max(int(lib.mla_default_num_parts(per_unit * h, max(1, num_cus)))
+                     for h in {max(1, active_h_q or h_q), h_q})
+    cap = int(lib.mla_metadata_capacity(units, max(1, target)))
+    meta = np.zeros(cap, dtype=np.int32)
+    info = MlaSchedInfo()
+    rc = lib.mla_get_metadata(sl.ctypes.data if batch else None, batch, s_q, h_q, h_kv, topk,
+                              active_h_q, int(num_cus), num_parts, meta.ctypes.data, cap,
+                              ctypes.byref(info))
+    _check(rc, "mla_get_metadata")
+    if rc == MLA_W_ACTIVE_FALLBACK:
+        warnings.warn(f"active_h_q={active_h_q} invalid for h_q={h_q}: all heads are computed")
+    meta = meta[:info.total_ints].copy()
+    meta_dev = torch.from_numpy(meta).to(device) if upload else None
+    return Metadata(info, meta, meta_dev, sparse=topk > 0, batch=batch, s_q=s_q, h_q=h_q, topk=topk)
+
+
+def mla_workspace_bytes(meta: Metadata, dv: int = 512) -> int:
+    return meta.workspace_bytes(dv)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _prep_outputs(q, meta, dv, workspace, out, lse):
+    B, s_q, h_q, _ = q.shape
+    if out is None:
+        out = torch.empty((B, s_q, h_q, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+    _need(out.shape == (B, s_q, h_q, dv) and out.dtype == torch.bfloat16 and out.is_contiguous(),
+          "out must be contiguous bf16 [B, s_q, h_q, dv]")
+    _need(lse.shape == (B, s_q, h_q) and lse.dtype == torch.float32 and lse.is_contiguous(),
+          "lse must be contiguous fp32 [B, s_q, h_q]")
+    need = meta.workspace_bytes(dv)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return out, lse, workspace, ws_bytes
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Metadata,
+                     causal: bool = False, softmax_scale: float | None = None,
+                     workspace=None, out=None, lse=None):
+    """Dense paged decode; returns (out [B, s_q, h_q, dv] bf16, lse [B, s_q, h_q] fp32)."""
+    lib = _load()
+    _need(q.dim() == 4 and kvcache.dim() == 4, "q is [B, s_q, h_q, d_qk], kvcache [blocks, 64, h_kv, d_qk]")
+    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
+    _need(q.is_cuda and kvcache.is_cuda and block_table.is_cuda and cache_seqlens.is_cuda,
+          "all tensors must be on the GPU")
+    _need(q.is_contiguous() and kvcache.is_contiguous() and block_table.is_contiguous()
+          and cache_seqlens.is_contiguous(), "tensors must be contiguous")
+    _need(block_table.dtype == torch.int32 and cache_seqlens.dtype == torch.int32,
+          "block_table and cache_seqlens must be int32")
+    _need(not meta.sparse, "metadata was built for sparse decode")
+    B, s_q, h_q, d_qk = q.shape
+    nblk, page, h_kv, d_kv = kvcache.shape
+    _need(d_kv == d_qk, "kvcache row width must equal q's d_qk")
+    _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
+    _need(cache_seqlens.shape == (B,), "cache_seqlens must be [B]")
+    segs = meta.segments
+    _need(len(segs) == 0 or int(segs[:, 2].max()) <= block_table.shape[1],
+          "cache_seqlens of the metadata need more blocks than block_table has columns")
+    if softmax_scale is None:
+        softmax_scale = d_qk ** -0.5
+    out, lse, workspace, ws_bytes = _prep_outputs(q, meta, dv, workspace, out, lse)
+    rc = lib.mla_decode_paged(_ptr(q), _ptr(kvcache), _ptr(block_table), _ptr(cache_seqlens), B,
+                              s_q, h_q, h_kv, d_qk, dv, nblk, page, block_table.shape[1],
+                              1 if causal else 0, float(softmax_scale), _ptr(meta.meta_dev),
+                              ctypes.byref(meta.info), _ptr(workspace), ws_bytes, _ptr(out),
+                              _ptr(lse), _stream(q.device))
+    _check(rc, "mla_decode_paged")
+    return out, lse
+
+
+def mla_decode_sparse(q, kvcache, indices, dv: int, meta: Metadata,
+                      softmax_scale: float | None = None, workspace=None, out=None, lse=None):
+    """Top-k sparse decode; heads past the metadata's active count are not written."""
+    lib = _load()
+    _need(q.dim() == 4 and kvcache.dim() == 4 and indices.dim() == 3, "bad ranks")
+    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
+    _need(indices.dtype == torch.int32, "indices must be int32")
+    _need(q.is_cuda and kvcache.is_cuda and indices.is_cuda, "all tensors must be on the GPU")
+    _need(q.is_contiguous() and kvcache.is_contiguous() and indices.is_contiguous(),
+          "tensors must be contiguous")
+    _need(meta.sparse, "metadata was built for dense decode")
+    B, s_q, h_q, d_qk = q.shape
+    nblk, page, h_kv, d_kv = kvcache.shape
+    _need(d_kv == d_qk, "kvcache row width must equal q's d_qk")
+    _need(indices.shape[:2] == (B, s_q), "indices must be [B, s_q, topk]")
+    topk = indices.shape[2]
+    _need(topk == meta.topk, f"indices topk {topk} != metadata topk {meta.topk}")
+    if softmax_scale is None:
+        softmax_scale = d_qk ** -0.5
+    out, lse, workspace, ws_bytes = _prep_outputs(q, meta, dv, workspace, out, lse)
+    rc = lib.mla_decode_sparse(_ptr(q), _ptr(kvcache), _ptr(indices), B, s_q, h_q, h_kv, d_qk, dv,
+                               nblk, page, topk, float(softmax_scale), _ptr(meta.meta_dev),
+                               ctypes.byref(meta.info), _ptr(workspace), ws_bytes, _ptr(out),
+                               _ptr(lse), _stream(q.device))
+    _check(rc, "mla_decode_sparse")
+    return out, lse
+
+
+# ---- the pages' call shape ------------------------------------------------
+
+def get_mla_metadata(cache_seqlens, num_q_tokens_per_head_k: int, num_heads_k: int,
+                     num_heads_q: int | None = None, is_fp8_kvcache: bool = False,
+                     topk: int | None = None, active_h_q: int = 0):
+    """The pages' ``get_mla_metadata(cache_seqlens, s_q*h_q//h_kv, h_kv[, h_q, is_fp8, topk])``.
+
+    Returns ``(tile_scheduler_metadata, num_splits)``: the :class:`Metadata`
+    object (pass it back as ``tile_scheduler_metadata``) and the cumulative
+    per-unit segment counts on the device."""
+    if is_fp8_kvcache:
+        raise NotImplementedError("FP8 KV cache is not built; the cache must be bf16")
+    rows = int(num_q_tokens_per_head_k)
+    if topk:
+        _need(num_heads_q is not None, "sparse metadata needs num_heads_q")
+        s_q = rows * num_heads_k // num_heads_q
+        meta = mla_get_metadata(cache_seqlens, s_q, num_heads_q, num_heads_k, topk=int(topk),
+                                active_h_q=active_h_q)
+    else:
+        h_q = num_heads_q if num_heads_q is not None else rows * num_heads_k
+        s_q = rows * num_heads_k // h_q
+        meta = mla_get_metadata(cache_seqlens, s_q, h_q, num_heads_k, active_h_q=active_h_q)
+    ns = torch.from_numpy(meta.num_splits.copy()).to(meta.meta_dev.device)
+    return meta, ns
+
+
+def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v: int,
+                           tile_scheduler_metadata: Metadata, num_splits=None,
+                           softmax_scale: float | None = None, causal: bool = False,
+                           is_fp8_kvcache: bool = False, indices=None):
+    """The pages' ``flash_mla_with_kvcache``; returns (out, lse)."""
+    if is_fp8_kvcache:
+        raise NotImplementedError("FP8 KV cache is not built; the cache must be bf16")
+    if indices is not None:
+        return mla_decode_sparse(q, k_cache, indices, head_dim_v, tile_scheduler_metadata,
+                                 softmax_scale=softmax_scale)
+    return mla_decode_paged(q, k_cache, block_table, cache_seqlens, head_dim_v,
+                            tile_scheduler_metadata, causal=causal, softmax_scale=softmax_scale)

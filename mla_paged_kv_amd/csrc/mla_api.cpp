@@ -1,0 +1,226 @@
+// C-ABI entry points of libmla.so: argument checks, workspace carving and
+// kernel launches for dense paged and top-k sparse MLA decode.  Every check
+// runs before anything is enqueued, so a rejected call touches no memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "mla.h"
+#include "mla_internal.h"
+#include "mla_kernels.h"
+
+namespace mla {
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+constexpr int32_t kPage = 64;
+constexpr int32_t kDV = 512;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Checks shared by the dense and sparse entry points.
+int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q, int32_t h_q,
+                 int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                 int32_t page_block_size, const int32_t* meta_dev, const mla_sched_info* info,
+                 void* workspace, size_t workspace_bytes, void* out, float* lse) {
+  if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || d_qk < 1 || dv < 1 || num_blocks < 0 ||
+      page_block_size < 1)
+    return set_error(MLA_E_INVAL, "decode: negative or zero shape");
+  if (h_kv != 1) return set_error(MLA_E_NOTSUP, "decode: h_kv=%d (only 1 is built)", h_kv);
+  if (page_block_size != kPage)
+    return set_error(MLA_E_NOTSUP, "decode: page_block_size=%d (only 64)", page_block_size);
+  if (d_qk != 576 && d_qk != 512) return set_error(MLA_E_NOTSUP, "decode: d_qk=%d", d_qk);
+  if (dv > d_qk) return set_error(MLA_E_INVAL, "decode: dv=%d > d_qk=%d", dv, d_qk);
+  if (dv != kDV) return set_error(MLA_E_NOTSUP, "decode: dv=%d (only 512)", dv);
+  if (info == nullptr) return set_error(MLA_E_INVAL, "decode: null info");
+  if (int64_t(num_blocks) * kPage > INT32_MAX)
+    return set_error(MLA_E_INVAL, "decode: num_blocks=%d too large", num_blocks);
+  if (info->num_parts < 0 || info->row_blocks < 1 || info->rows < 1 || info->total_slots < 0 ||
+      info->num_split_units < 0 || info->total_ints < kHeaderInts)
+    return set_error(MLA_E_INVAL, "decode: malformed metadata header");
+  if (info->row_blocks != (info->rows + 63) / 64)
+    return set_error(MLA_E_INVAL, "decode: metadata row_blocks inconsistent");
+  if (batch == 0) return MLA_OK;
+  if (!q || !kvcache || !meta_dev || !out || !lse)
+    return set_error(MLA_E_INVAL, "decode: null q/kvcache/meta/out/lse");
+  if (!aligned(q, 16) || !aligned(kvcache, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return set_error(MLA_E_INVAL, "decode: q/kvcache/out need 16-byte, lse 4-byte alignment");
+  if (num_blocks < 1) return set_error(MLA_E_INVAL, "decode: empty kvcache");
+  const size_t need = mla_workspace_bytes(info, dv);
+  if (need > 0) {
+    if (!workspace) return set_error(MLA_E_INVAL, "decode: metadata has splits, workspace is null");
+    if (!aligned(workspace, 256)) return set_error(MLA_E_INVAL, "decode: workspace not 256-aligned");
+    if (workspace_bytes < need)
+      return set_error(MLA_E_NOSPC, "decode: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  }
+  (void)s_q;
+  (void)h_q;
+  return MLA_OK;
+}
+
+int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, void* workspace,
+           int32_t dv, void* stream) {
+  const size_t o_bytes = size_t(info->total_slots) * info->rows * dv * sizeof(float);
+  kp.ws_o = static_cast<float*>(workspace);
+  kp.ws_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(o_bytes))
+                        : nullptr;
+  kp.num_parts = info->num_parts;
+  kp.row_blocks = info->row_blocks;
+  kp.rows = info->rows;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_splitkv(kp, d_qk, sparse, st);
+  if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
+  if (info->num_split_units > 0) {
+    CombineParams cp;
+    cp.meta = kp.meta;
+    cp.ws_o = kp.ws_o;
+    cp.ws_lse = kp.ws_lse;
+    cp.out = kp.out;
+    cp.lse = kp.lse;
+    cp.off_num_splits = info->off_num_splits;
+    cp.off_split_list = info->off_split_list;
+    cp.num_split_units = info->num_split_units;
+    cp.rows = info->rows;
+    cp.s_q = kp.s_q;
+    cp.h_q = kp.h_q;
+    cp.heads = kp.heads;
+    cp.sparse = sparse ? 1 : 0;
+    e = launch_combine(cp, st);
+    if (e != hipSuccess) return set_error(MLA_E_HIP, "combine launch: %s", hipGetErrorString(e));
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+}  // namespace mla
+
+extern "C" {
+
+int32_t mla_version(void) { return 0x00010000; }
+
+const char* mla_strerror(int code) {
+  switch (code) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_W_ACTIVE_FALLBACK: return "MLA_W_ACTIVE_FALLBACK";
+    case MLA_E_INVAL: return "MLA_E_INVAL";
+    case MLA_E_NOTSUP: return "MLA_E_NOTSUP";
+    case MLA_E_NOSPC: return "MLA_E_NOSPC";
+    case MLA_E_HIP: return "MLA_E_HIP";
+    default: return "MLA_E_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return mla::g_last_error; }
+
+size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v) {
+  if (info == nullptr || info->total_slots <= 0 || info->rows <= 0 || d_v <= 0) return 0;
+  const size_t o = size_t(info->total_slots) * info->rows * d_v * sizeof(float);
+  const size_t l = size_t(info->total_slots) * info->rows * sizeof(float);
+  return mla::align256(o) + mla::align256(l);
+}
+
+int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_table,
+                     const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                     int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                     int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                     float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
+                     void* workspace, size_t workspace_bytes, void* out, float* lse,
+                     void* stream) {
+  using namespace mla;
+  clear_error();
+  int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
+                        meta_dev, info, workspace, workspace_bytes, out, lse);
+  if (rc != MLA_OK || batch == 0) return rc;
+  if (!block_table || !cache_seqlens) return set_error(MLA_E_INVAL, "decode_paged: null block_table/seqlens");
+  if (bt_stride < 1) return set_error(MLA_E_INVAL, "decode_paged: bt_stride=%d", bt_stride);
+  if (causal != 0 && causal != 1) return set_error(MLA_E_INVAL, "decode_paged: causal=%d", causal);
+  if (!std::isfinite(softmax_scale)) return set_error(MLA_E_INVAL, "decode_paged: softmax_scale not finite");
+  if (info->num_units != batch)
+    return set_error(MLA_E_INVAL, "decode_paged: metadata built for %d units, batch=%d (dense mode?)",
+                     info->num_units, batch);
+  if (info->rows % s_q != 0)
+    return set_error(MLA_E_INVAL, "decode_paged: metadata rows %d not a multiple of s_q=%d", info->rows, s_q);
+  const int32_t heads = info->rows / s_q;
+  if (heads < 1 || heads > h_q)
+    return set_error(MLA_E_INVAL, "decode_paged: metadata heads %d outside [1, h_q=%d]", heads, h_q);
+
+  SplitKVParams kp{};
+  kp.q = static_cast<const uint16_t*>(q);
+  kp.kv = static_cast<const uint16_t*>(kvcache);
+  kp.block_table = block_table;
+  kp.seqlens = cache_seqlens;
+  kp.indices = nullptr;
+  kp.meta = meta_dev;
+  kp.out = static_cast<uint16_t*>(out);
+  kp.lse = lse;
+  kp.s_q = s_q;
+  kp.h_q = h_q;
+  kp.heads = heads;
+  kp.bt_stride = bt_stride;
+  kp.num_rows = num_blocks * kPage;
+  kp.topk = 0;
+  kp.causal = causal;
+  kp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launch(kp, info, d_qk, false, workspace, dv, stream);
+}
+
+int mla_decode_sparse(const void* q, const void* kvcache, const int32_t* indices,
+                      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                      int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                      float softmax_scale, const int32_t* meta_dev,
+                      const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                      void* out, float* lse, void* stream) {
+  using namespace mla;
+  clear_error();
+  int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
+                        meta_dev, info, workspace, workspace_bytes, out, lse);
+  if (rc != MLA_OK || batch == 0) return rc;
+  if (!indices) return set_error(MLA_E_INVAL, "decode_sparse: null indices");
+  if (topk < 1) return set_error(MLA_E_INVAL, "decode_sparse: topk=%d", topk);
+  if (!std::isfinite(softmax_scale)) return set_error(MLA_E_INVAL, "decode_sparse: softmax_scale not finite");
+  if (int64_t(info->num_units) != int64_t(batch) * s_q)
+    return set_error(MLA_E_INVAL, "decode_sparse: metadata built for %d units, batch*s_q=%lld (sparse mode?)",
+                     info->num_units, (long long)batch * s_q);
+  const int32_t heads = info->rows;
+  if (heads < 1 || heads > h_q)
+    return set_error(MLA_E_INVAL, "decode_sparse: metadata heads %d outside [1, h_q=%d]", heads, h_q);
+
+  SplitKVParams kp{};
+  kp.q = static_cast<const uint16_t*>(q);
+  kp.kv = static_cast<const uint16_t*>(kvcache);
+  kp.block_table = nullptr;
+  kp.seqlens = nullptr;
+  kp.indices = indices;
+  kp.meta = meta_dev;
+  kp.out = static_cast<uint16_t*>(out);
+  kp.lse = lse;
+  kp.s_q = s_q;
+  kp.h_q = h_q;
+  kp.heads = heads;
+  kp.bt_stride = 0;
+  kp.num_rows = num_blocks * kPage;
+  kp.topk = topk;
+  kp.causal = 0;
+  kp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launch(kp, info, d_qk, true, workspace, dv, stream);
+}
+
+}  // extern "C"

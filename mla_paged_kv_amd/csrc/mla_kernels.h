@@ -1,0 +1,48 @@
+// Kernel parameter blocks and launchers of libmla.so (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace mla {
+
+constexpr int kMetaHeaderInts = 16;  // int32 header ahead of part_ptr in the metadata
+
+struct SplitKVParams {
+  const uint16_t* q;           // [batch, s_q, h_q, d_qk] bf16
+  const uint16_t* kv;          // [num_blocks * 64, d_qk] bf16 (h_kv = 1)
+  const int32_t* block_table;  // dense: [batch, bt_stride]
+  const int32_t* seqlens;      // dense: [batch]
+  const int32_t* indices;      // sparse: [batch * s_q, topk]
+  const int32_t* meta;         // device copy of the scheduler metadata
+  uint16_t* out;               // [batch, s_q, h_q, 512] bf16
+  float* lse;                  // [batch, s_q, h_q] fp32 (natural log)
+  float* ws_o;                 // [slots, rows, 512] fp32 partial outputs
+  float* ws_lse;               // [slots, rows] fp32 partial LSE (base 2)
+  int32_t s_q, h_q;
+  int32_t heads;      // active heads (first `heads` of h_q)
+  int32_t rows;       // query rows per unit
+  int32_t bt_stride;
+  int32_t num_rows;   // num_blocks * 64 (sparse index bound)
+  int32_t topk;
+  int32_t causal;
+  int32_t num_parts, row_blocks;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+struct CombineParams {
+  const int32_t* meta;
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* out;
+  float* lse;
+  int32_t off_num_splits, off_split_list, num_split_units;
+  int32_t rows, s_q, h_q, heads;
+  int32_t sparse;
+};
+
+hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+}  // namespace mla

@@ -91,8 +91,21 @@ def visible_len(L: int, s_q: int, i: int, causal: bool) -> int:
     return max(0, min(L, L - s_q + i + 1))
 
 
+def _gather_f64(kv, rows_index):
+    """kv[rows_index] as float64, converting only the gathered rows."""
+    try:
+        import torch
+
+        if isinstance(kv, torch.Tensor):
+            ix = tuple(torch.as_tensor(np.asarray(a), dtype=torch.long) for a in rows_index)
+            return kv[ix].to(dtype=torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(kv[rows_index], dtype=np.float64)
+
+
 def ref_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, causal: bool,
-                     softmax_scale: float, heads=None):
+                     softmax_scale: float, heads=None, batches=None):
     """Dense paged MLA decode, FP64.
 
     q            [B, s_q, h_q, d_qk]
@@ -102,26 +115,27 @@ def ref_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, causal: bo
     cache_seqlens[B] int; tokens in the cache of request b (the s_q new tokens
                  included)
     heads        optional iterable of head indices to compute (default: all)
+    batches      optional iterable of requests to compute (default: all)
 
     Returns (O [B, s_q, h_q, dv] float64, LSE [B, s_q, h_q] float64, natural
-    log).  Heads not in ``heads`` are left as NaN.
+    log).  Entries not computed are NaN.  Only the cache rows a request can
+    see are read (and converted to float64).
     """
     qf = _to_f64(q)
-    kv = _to_f64(kvcache)
     bt = _to_i64(block_table)
     sl = _to_i64(cache_seqlens)
     B, s_q, h_q, d_qk = qf.shape
-    _, page, h_kv, d_kv = kv.shape
+    _, page, h_kv, d_kv = kvcache.shape
     assert d_kv == d_qk and h_q % h_kv == 0 and dv <= d_qk
     group = h_q // h_kv
     head_list = list(range(h_q)) if heads is None else list(heads)
     O = np.full((B, s_q, h_q, dv), np.nan)
     LSE = np.full((B, s_q, h_q), np.nan)
-    for b in range(B):
+    for b in (range(B) if batches is None else batches):
         L = int(sl[b])
         pos = np.arange(L)
         phys = bt[b, pos // page] if L > 0 else np.zeros(0, dtype=np.int64)
-        rows = kv[phys, pos % page]  # [L, h_kv, d_qk], logical order
+        rows = _gather_f64(kvcache, (phys, pos % page))  # [L, h_kv, d_qk], logical order
         for i in range(s_q):
             n = visible_len(L, s_q, i, causal)
             for hk in range(h_kv):
@@ -134,38 +148,39 @@ def ref_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, causal: bo
     return O, LSE
 
 
-def ref_decode_sparse(q, kvcache, indices, dv: int, softmax_scale: float, heads=None):
+def ref_decode_sparse(q, kvcache, indices, dv: int, softmax_scale: float, heads=None,
+                      batches=None):
     """Top-k sparse MLA decode, FP64.
 
     q        [B, s_q, h_q, d_qk]
-    kvcache  [num_blocks, page, h_kv, d_qk]; viewed as [num_blocks*page, h_kv, d_qk]
+    kvcache  [num_blocks, page, h_kv, d_qk]; row e = block e // page, offset e % page
     indices  [B, s_q, topk] int; entry = block*page + offset, invalid if < 0 or
              >= num_blocks*page (those are dropped)
     heads    optional iterable of heads to compute (default: all); sparse decode
              computes only the first ``active_h_q`` heads.
+    batches  optional iterable of requests to compute (default: all)
 
-    Returns (O [B, s_q, h_q, dv], LSE [B, s_q, h_q]); heads not computed are NaN.
+    Returns (O [B, s_q, h_q, dv], LSE [B, s_q, h_q]); entries not computed are NaN.
     """
     qf = _to_f64(q)
-    kv = _to_f64(kvcache)
     idx = _to_i64(indices)
     B, s_q, h_q, d_qk = qf.shape
-    nblk, page, h_kv, d_kv = kv.shape
+    nblk, page, h_kv, d_kv = kvcache.shape
     assert d_kv == d_qk and h_q % h_kv == 0 and dv <= d_qk
-    flat = kv.reshape(nblk * page, h_kv, d_qk)
     group = h_q // h_kv
     head_list = list(range(h_q)) if heads is None else list(heads)
     O = np.full((B, s_q, h_q, dv), np.nan)
     LSE = np.full((B, s_q, h_q), np.nan)
-    for b in range(B):
+    for b in (range(B) if batches is None else batches):
         for i in range(s_q):
             sel = idx[b, i]
             sel = sel[(sel >= 0) & (sel < nblk * page)]
+            rows = _gather_f64(kvcache, (sel // page, sel % page))  # [n, h_kv, d_qk]
             for hk in range(h_kv):
                 hs = [h for h in head_list if h // group == hk]
                 if not hs:
                     continue
-                o, lse = ref_attend_rows(qf[b, i, hs, :], flat[sel, hk, :], dv, softmax_scale)
+                o, lse = ref_attend_rows(qf[b, i, hs, :], rows[:, hk, :], dv, softmax_scale)
                 O[b, i, hs, :] = o
                 LSE[b, i, hs] = lse
     return O, LSE

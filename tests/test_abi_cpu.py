@@ -1,0 +1,218 @@
+"""CPU-side checks of libmla.so: exports, the host scheduler, argument validation.
+
+No GPU is needed: the scheduler is host code, and every decode call below is
+rejected by argument validation before anything is enqueued (the pointers
+passed are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import mla_paged_kv_amd as mla
+from mla_paged_kv_amd import _binding as B
+from oracle.schedule import ref_num_parts, ref_schedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.lib_path()):
+        from mla_paged_kv_amd.build import build
+        build()
+    return B._load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ["mla_get_metadata", "mla_decode_paged", "mla_decode_sparse", "mla_workspace_bytes",
+              "mla_strerror", "mla_last_error", "mla_version", "mla_default_num_parts",
+              "mla_metadata_capacity"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mla_\w+)$", out, flags=re.M))
+    for n in header_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version_and_strerror(lib):
+    assert lib.mla_version() == 0x00010000
+    assert lib.mla_strerror(0) == b"MLA_OK"
+    assert lib.mla_strerror(-2) == b"MLA_E_NOTSUP"
+    assert lib.mla_strerror(1) == b"MLA_W_ACTIVE_FALLBACK"
+
+
+def _cpp_schedule(lens, P, rows):
+    m = mla.mla_get_metadata(np.asarray(lens, dtype=np.int32), 1, rows, num_parts=P, num_cus=0,
+                             upload=False)
+    return m.meta_host
+
+
+@settings(max_examples=300, deadline=None)
+@given(lens=st.lists(st.integers(0, 20000), min_size=0, max_size=60), P=st.integers(1, 1100),
+       rows=st.integers(1, 256))
+def test_cpp_scheduler_bit_exact_vs_reference(lib, lens, P, rows):
+    np.testing.assert_array_equal(_cpp_schedule(lens, P, rows), ref_schedule(lens, P, rows))
+
+
+def test_cpp_scheduler_bit_exact_at_config_shapes(lib):
+    from synth.configs import CONFIGS, rng_for
+    for k, spec in CONFIGS.items():
+        if spec["kind"] == "dense":
+            lens = spec.get("seqlens")
+            if lens is None:
+                lens = spec["seqlen_sampler"](rng_for(1000 + k))
+            rows = spec["s_q"] * spec["h_q"]
+            units = lens
+        else:
+            rows = spec["active_h_q"]
+            units = [spec["topk"]] * (spec["B"] * spec["s_q"])
+        for cus in (256, 304, 80):
+            P = ref_num_parts(rows, cus)
+            assert lib.mla_default_num_parts(rows, cus) == P
+            np.testing.assert_array_equal(_cpp_schedule(units, P, rows), ref_schedule(units, P, rows))
+
+
+def test_sparse_mode_units_are_query_tokens(lib):
+    m = mla.mla_get_metadata([5, 5, 5], 2, 64, topk=300, active_h_q=16, num_cus=256, upload=False)
+    assert m.num_units == 6 and m.rows == 16
+    np.testing.assert_array_equal(m.meta_host, ref_schedule([300] * 6, ref_num_parts(16, 256), 16))
+
+
+def test_active_heads_fail_closed(lib):
+    with pytest.warns(UserWarning):
+        m = mla.mla_get_metadata(None or [10], 1, 64, topk=64, active_h_q=12, num_cus=256, upload=False)
+    assert m.rows == 64
+    m = mla.mla_get_metadata([10], 1, 64, topk=64, active_h_q=16, num_cus=256, upload=False)
+    assert m.rows == 16
+    m = mla.mla_get_metadata([10], 2, 32, active_h_q=8, num_cus=256, upload=False)
+    assert m.rows == 16 and m.heads == 8
+    with pytest.warns(UserWarning):
+        m = mla.mla_get_metadata([10], 1, 64, topk=64, active_h_q=72, num_cus=256, upload=False)
+    assert m.rows == 64
+
+
+def _raw_meta(lib, lens, P=4, rows=16):
+    cap = lib.mla_metadata_capacity(len(lens), P)
+    meta = np.zeros(cap, dtype=np.int32)
+    info = B.MlaSchedInfo()
+    sl = np.asarray(lens, dtype=np.int32)
+    rc = lib.mla_get_metadata(sl.ctypes.data, len(lens), 1, rows, 1, 0, 0, 0, P,
+                              meta.ctypes.data, cap, ctypes.byref(info))
+    return rc, meta, info
+
+
+def test_get_metadata_errors(lib):
+    info = B.MlaSchedInfo()
+    meta = np.zeros(8, dtype=np.int32)
+    sl = np.asarray([100, 200], dtype=np.int32)
+    # capacity too small
+    assert lib.mla_get_metadata(sl.ctypes.data, 2, 1, 16, 1, 0, 0, 0, 4, meta.ctypes.data, 8,
+                                ctypes.byref(info)) == -3
+    big = np.zeros(1000, dtype=np.int32)
+    # negative length
+    neg = np.asarray([100, -1], dtype=np.int32)
+    assert lib.mla_get_metadata(neg.ctypes.data, 2, 1, 16, 1, 0, 0, 0, 4, big.ctypes.data, 1000,
+                                ctypes.byref(info)) == -1
+    assert b"cache_seqlens[1]" in lib.mla_last_error()
+    # h_q not a multiple of h_kv
+    assert lib.mla_get_metadata(sl.ctypes.data, 2, 1, 15, 2, 0, 0, 0, 4, big.ctypes.data, 1000,
+                                ctypes.byref(info)) == -1
+    # neither num_cus nor num_parts
+    assert lib.mla_get_metadata(sl.ctypes.data, 2, 1, 16, 1, 0, 0, 0, 0, big.ctypes.data, 1000,
+                                ctypes.byref(info)) == -1
+    # dense mode without lengths
+    assert lib.mla_get_metadata(None, 2, 1, 16, 1, 0, 0, 0, 4, big.ctypes.data, 1000,
+                                ctypes.byref(info)) == -1
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _paged(lib, info, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, batch=2, s_q=1, h_q=16, h_kv=1, d_qk=576, dv=512,
+             nblk=8, page=64, bt_stride=4, causal=0, scale=0.04, meta=FAKE, ws=None, ws_bytes=0,
+             out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_paged(a["q"], a["kv"], a["bt"], a["sl"], a["batch"], a["s_q"], a["h_q"],
+                                a["h_kv"], a["d_qk"], a["dv"], a["nblk"], a["page"], a["bt_stride"],
+                                a["causal"], a["scale"], a["meta"], ctypes.byref(info), a["ws"],
+                                a["ws_bytes"], a["out"], a["lse"], None)
+
+
+def test_decode_paged_rejects_bad_arguments(lib):
+    rc, meta, info = _raw_meta(lib, [64, 200], P=512, rows=16)
+    assert rc == 0 and info.total_slots > 0
+    assert _paged(lib, info, h_kv=2, h_q=16) == -2          # h_kv != 1 not built
+    assert _paged(lib, info, page=32) == -2                 # page size
+    assert _paged(lib, info, d_qk=192) == -2                # MHA-mode head dims not built
+    assert _paged(lib, info, dv=128, d_qk=576) == -2
+    assert _paged(lib, info, dv=600) == -1                  # dv > d_qk
+    assert _paged(lib, info, q=FAKE + 2) == -1              # misaligned
+    assert _paged(lib, info, ws=None, ws_bytes=0) == -1     # splits need a workspace
+    assert _paged(lib, info, ws=FAKE, ws_bytes=16) == -3    # workspace too small
+    ws = lib.mla_workspace_bytes(ctypes.byref(info), 512)
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, batch=3) == -1   # metadata for 2 units
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, s_q=3) == -1     # rows 16 not a multiple of 3
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, h_q=8) == -1     # 16 heads > h_q
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, causal=2) == -1
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, scale=float("nan")) == -1
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, bt=None) == -1
+    assert _paged(lib, info, ws=FAKE, ws_bytes=ws, bt_stride=0) == -1
+    bad = B.MlaSchedInfo.from_buffer_copy(info)
+    bad.row_blocks = 7
+    assert _paged(lib, bad, ws=FAKE, ws_bytes=ws) == -1     # malformed header
+    assert b"row_blocks" in lib.mla_last_error()
+
+
+def test_decode_sparse_rejects_bad_arguments(lib):
+    cap = lib.mla_metadata_capacity(2, 8)
+    meta = np.zeros(cap, dtype=np.int32)
+    info = B.MlaSchedInfo()
+    assert lib.mla_get_metadata(None, 2, 1, 64, 1, 2048, 16, 0, 8, meta.ctypes.data, cap,
+                                ctypes.byref(info)) == 0
+    ws = lib.mla_workspace_bytes(ctypes.byref(info), 512)
+
+    def call(**kw):
+        a = dict(q=FAKE, kv=FAKE, ix=FAKE, batch=2, s_q=1, h_q=64, h_kv=1, d_qk=512, dv=512,
+                 nblk=64, page=64, topk=2048, scale=0.04, meta=FAKE, ws=FAKE, ws_bytes=ws,
+                 out=FAKE, lse=FAKE)
+        a.update(kw)
+        return lib.mla_decode_sparse(a["q"], a["kv"], a["ix"], a["batch"], a["s_q"], a["h_q"],
+                                     a["h_kv"], a["d_qk"], a["dv"], a["nblk"], a["page"],
+                                     a["topk"], a["scale"], a["meta"], ctypes.byref(info),
+                                     a["ws"], a["ws_bytes"], a["out"], a["lse"], None)
+
+    assert call(ix=None) == -1
+    assert call(topk=0) == -1
+    assert call(batch=1) == -1       # metadata for 2 query tokens
+    assert call(h_q=8) == -1         # 16 active heads > h_q
+    assert call(d_qk=576, dv=576) == -2
+    assert call(ws_bytes=ws - 4) == -3
+    assert call(nblk=1 << 26) == -1  # rows would overflow int32
+
+
+def test_workspace_bytes(lib):
+    rc, meta, info = _raw_meta(lib, [64, 200], P=512, rows=16)
+    n = lib.mla_workspace_bytes(ctypes.byref(info), 512)
+    slots, rows = info.total_slots, info.rows
+    assert n == -(-slots * rows * 512 * 4 // 256) * 256 + -(-slots * rows * 4 // 256) * 256
+    rc, meta, info = _raw_meta(lib, [64, 64], P=2, rows=16)
+    assert info.total_slots == 0 and lib.mla_workspace_bytes(ctypes.byref(info), 512) == 0
