@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of paged MLA decode on one MI355X: TFLOPS and HBM GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step is one decode call over the whole batch of the workload: the split-KV
+kernel then the LSE combine, on inputs already resident in HBM.  The tile
+scheduler runs once per decode step and its metadata is reused by every layer
+(the pages' call pattern), so it is timed separately on the host
+(``metadata_us``); ``with_metadata`` reports the rate when every step also
+rebuilds and uploads the metadata.  The cache is rotated over enough copies
+that one step's working set is not served from the 256 MB Infinity Cache of
+the previous step.
+
+Algorithmic work (what the method must do, not padded work):
+  FLOP  = sum over (query row, visible key) of 2 * (d_qk + d_v)
+  bytes = every visible cache row once per request (d_qk * 2 B; the value is
+          inside it) + q, O (bf16) and LSE (fp32) of the computed heads
+          + block-table entries (or indices) read + sequence lengths.
+The split workspace traffic is overhead and is not counted.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on, around each kernel of every timed step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512) on 1 GPU"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+KERNEL_SOURCES = ["mla_paged_kv_amd/csrc/mla_kernels.hip", "mla_paged_kv_amd/csrc/mla_kernels.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(case) -> dict:
+    """Integer accounting of the work the method must do (see module docstring)."""
+    s_q, d_qk, d_v = case["s_q"], case["d_qk"], case["d_v"]
+    B = case["q"].shape[0]
+    if case["sparse"]:
+        heads = case["active_h_q"]
+        idx = case["indices"]
+        nrows = case["kvcache"].shape[0] * case["kvcache"].shape[1]
+        valid = ((idx >= 0) & (idx < nrows)).sum().item()
+        flop = valid * heads * 2 * (d_qk + d_v)
+        kv_bytes = valid * d_qk * 2
+        meta_bytes = idx.numel() * 4
+        keys = valid
+    else:
+        heads = case["h_q"]
+        sl = case["cache_seqlens"].tolist()
+        keys = 0
+        for L in sl:
+            for i in range(s_q):
+                keys += max(0, min(L, L - s_q + i + 1)) if case["causal"] else L
+        flop = keys * heads * 2 * (d_qk + d_v)
+        kv_bytes = sum(sl) * d_qk * 2
+        meta_bytes = sum((L + 63) // 64 for L in sl) * 4 + B * 4
+    q_bytes = B * s_q * heads * d_qk * 2
+    o_bytes = B * s_q * heads * (d_v * 2 + 4)
+    return dict(flop=flop, bytes=kv_bytes + q_bytes + o_bytes + meta_bytes, kv_bytes=kv_bytes,
+                keys=keys)
+
+
+def cpu_baseline(case, min_seconds: float, max_passes: int = 8) -> dict:
+    """The FP64 oracle as it stands, on the host cores, over whole passes of
+    the workload (at least one, until ``min_seconds`` have elapsed)."""
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max([p["num_threads"] for p in blas] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    work = algorithmic_work(case)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        if case["sparse"]:
+            oracle.ref_decode_sparse(case["q"], case["kvcache"], case["indices"], case["d_v"],
+                                     case["softmax_scale"], heads=range(case["active_h_q"]))
+        else:
+            oracle.ref_decode_paged(case["q"], case["kvcache"], case["block_table"],
+                                    case["cache_seqlens"], case["d_v"], case["causal"],
+                                    case["softmax_scale"])
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    return {"value": round(work["flop"] * passes / dt / 1e12, 6), "unit": "TFLOPS",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"whole workload x {passes} pass(es), {dt:.1f} s, float64 numpy "
+                      f"(BLAS threads {cores}, host cpus {os.cpu_count()})"}
+
+
+def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600) -> dict:
+    import torch
+
+    import mla_paged_kv_amd as mla
+    from synth.configs import make_config
+
+    case = make_config(k)
+    work = algorithmic_work(case)
+    dev = torch.device("cuda", 0)
+    q = case["q"].to(dev)
+    kv0 = case["kvcache"].to(dev)
+    pool_mb = kv0.numel() * 2 / 2**20
+    copies = max(1, min(8, math.ceil(rotate_mb / max(pool_mb, 1e-9))))
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    bt = case["block_table"].to(dev)
+    sl = case["cache_seqlens"].to(dev)
+    idx = case["indices"].to(dev) if case["sparse"] else None
+
+    def get_meta():
+        if case["sparse"]:
+            return mla.mla_get_metadata(case["cache_seqlens"], case["s_q"], case["h_q"],
+                                        topk=case["topk"], active_h_q=case["active_h_q"], device=dev)
+        return mla.mla_get_metadata(case["cache_seqlens"], case["s_q"], case["h_q"], device=dev)
+
+    t0 = time.perf_counter()
+    for _ in range(20):
+        meta = get_meta()
+    torch.cuda.synchronize()
+    metadata_us = (time.perf_counter() - t0) / 20 * 1e6
+
+    B, s_q, h_q = case["q"].shape[:3]
+    out = torch.empty((B, s_q, h_q, case["d_v"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    ws_bytes = meta.workspace_bytes(case["d_v"])
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def split(kv, m):
+        if case["sparse"]:
+            mla.mla_decode_sparse(q, kv, idx, case["d_v"], m, softmax_scale=case["softmax_scale"],
+                                  workspace=ws, out=out, lse=lse, stage="split")
+        else:
+            mla.mla_decode_paged(q, kv, bt, sl, case["d_v"], m, causal=case["causal"],
+                                 softmax_scale=case["softmax_scale"], workspace=ws, out=out,
+                                 lse=lse, stage="split")
+
+    def combine(m):
+        mla.mla_combine(m, out, lse, ws, case["d_v"])
+
+    for i in range(warmup):
+        split(kvs[i % copies], meta)
+        combine(meta)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        a, b, c = ev[i]
+        a.record()
+        split(kvs[i % copies], meta)
+        b.record()
+        combine(meta)
+        c.record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / steps
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+
+    # rate with the scheduler and its upload inside every step
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        m = get_meta()
+        split(kvs[i % copies], m)
+        combine(m)
+    torch.cuda.synchronize()
+    ms_with_meta = (time.perf_counter() - t0) * 1e3 / steps
+
+    ai = work["flop"] / work["bytes"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if ai >= ridge else "hbm"
+    if bound == "hbm":
+        achieved = work["bytes"] / (split_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = work["flop"] / (split_ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    res = dict(
+        case=case, work=work, ms_step=ms_step, split_ms=split_ms, combine_ms=comb_ms,
+        tflops=work["flop"] / (ms_step * 1e-3) / 1e12,
+        gbs=work["bytes"] / (ms_step * 1e-3) / 1e9,
+        metadata_us=metadata_us, ms_with_meta=ms_with_meta,
+        roofline=dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
+                      frac=round(achieved / peak, 4), traffic=None),
+        sched=dict(num_parts=meta.num_parts, row_blocks=meta.row_blocks,
+                   max_splits=meta.max_splits, split_units=meta.num_split_units,
+                   workspace_mb=round(ws_bytes / 2**20, 2)),
+        copies=copies,
+    )
+    return res
+
+
+def load_traffic(k: int, steps_ms: float):
+    """HBM traffic per launch of the split-KV kernel from committed counter
+    summaries, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"splitkv_traffic_workload{k}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="seeded workload (2 = varlen decode, h_q=128: the headline)")
+    ap.add_argument("--others", default="3,4,5",
+                    help="extra workloads timed into 'other_workloads' ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
+                                   "design note, not an implemented path", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    r = bench_workload(args.workload, args.steps, args.warmup)
+    case = r["case"]
+    traffic = load_traffic(args.workload, r["split_ms"])
+    r["roofline"]["traffic"] = traffic
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case["name"], "batch": int(case["q"].shape[0]),
+                   "s_q": case["s_q"], "h_q": case["h_q"], "d_qk": case["d_qk"],
+                   "d_v": case["d_v"], "causal": case["causal"],
+                   "visible_keys": r["work"]["keys"], "parallelism": "single GPU"},
+        "hbm_gbps": round(r["gbs"], 1),
+        "frac_mfma_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+        "frac_hbm_peak": round(r["gbs"] / PEAK_HBM_GBS, 4),
+        "kernels_ms": {"splitkv": round(r["split_ms"], 5), "combine": round(r["combine_ms"], 5)},
+        "metadata_us": round(r["metadata_us"], 1),
+        "with_metadata": {"ms_per_step": round(r["ms_with_meta"], 5),
+                          "tflops": round(r["work"]["flop"] / (r["ms_with_meta"] * 1e-3) / 1e12, 3)},
+        "schedule": r["sched"],
+        "algorithmic": {"flop": r["work"]["flop"], "bytes": r["work"]["bytes"]},
+        "cache_copies_rotated": r["copies"],
+        "roofline": r["roofline"],
+        "kernel_source_hash": kernel_hash(),
+    }
+    others = {}
+    for k in [int(x) for x in args.others.split(",") if x.strip()]:
+        if k == args.workload:
+            continue
+        o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2))
+        others[str(k)] = {
+            "workload": o["case"]["name"], "ms_per_step": round(o["ms_step"], 5),
+            "tflops": round(o["tflops"], 2), "hbm_gbps": round(o["gbs"], 1),
+            "frac_mfma_peak": round(o["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "frac_hbm_peak": round(o["gbs"] / PEAK_HBM_GBS, 4),
+            "kernels_ms": {"splitkv": round(o["split_ms"], 5), "combine": round(o["combine_ms"], 5)},
+            "roofline": o["roofline"], "schedule": o["sched"],
+        }
+        del o
+        torch.cuda.empty_cache()
+    if others:
+        line["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -193,6 +193,41 @@ int mla_decode_sparse(const void* q, const void* kvcache, const int32_t* indices
                       const mla_sched_info* info, void* workspace, size_t workspace_bytes,
                       void* out, float* lse, void* stream);
 
+/*
+ * The two stages of a decode call, for callers that schedule them separately
+ * (the pages name the split-KV and combine kernels as the two hot kernels of
+ * sparse decode: DeepLink-org fork, background section).  A decode call is
+ * exactly mla_splitkv_* followed by mla_combine on the same stream, with the
+ * same metadata, workspace, out and lse.
+ *
+ * mla_splitkv_paged / mla_splitkv_sparse: same arguments and checks as
+ *   mla_decode_paged / mla_decode_sparse.  Writes out/lse of every unit that
+ *   the metadata does not split, and the fp32 partials of split units into
+ *   the workspace.
+ * mla_combine: LSE-merges the workspace partials of every split unit into
+ *   out/lse, for the active rows only (the fork's active-head combine).
+ *   sparse = 0/1 says which mode the metadata was built for; batch, s_q, h_q
+ *   as in the decode call.  Nothing is launched when no unit is split.
+ */
+int mla_splitkv_paged(const void* q, const void* kvcache, const int32_t* block_table,
+                      const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                      int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                      int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                      float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      void* stream);
+
+int mla_splitkv_sparse(const void* q, const void* kvcache, const int32_t* indices,
+                       int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                       int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                       float softmax_scale, const int32_t* meta_dev,
+                       const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                       void* out, float* lse, void* stream);
+
+int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,
+                int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
+                size_t workspace_bytes, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     flash_mla_with_kvcache,
     get_mla_metadata,
     lib_path,
+    mla_combine,
     mla_decode_paged,
     mla_decode_sparse,
     mla_get_metadata,
@@ -34,6 +35,7 @@ __all__ = [
     "flash_mla_with_kvcache",
     "get_mla_metadata",
     "lib_path",
+    "mla_combine",
     "mla_decode_paged",
     "mla_decode_sparse",
     "mla_get_metadata",

@@ -70,6 +70,12 @@ def _load():
     lib.mla_decode_sparse.restype = ctypes.c_int
     lib.mla_decode_sparse.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                       ctypes.c_float, vp, pinfo, vp, sz, vp, vp, vp]
+    lib.mla_splitkv_paged.restype = ctypes.c_int
+    lib.mla_splitkv_paged.argtypes = lib.mla_decode_paged.argtypes
+    lib.mla_splitkv_sparse.restype = ctypes.c_int
+    lib.mla_splitkv_sparse.argtypes = lib.mla_decode_sparse.argtypes
+    lib.mla_combine.restype = ctypes.c_int
+    lib.mla_combine.argtypes = [vp, pinfo, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -197,9 +203,13 @@ def _stream(device):
 
 def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Metadata,
                      causal: bool = False, softmax_scale: float | None = None,
-                     workspace=None, out=None, lse=None):
-    """Dense paged decode; returns (out [B, s_q, h_q, dv] bf16, lse [B, s_q, h_q] fp32)."""
+                     workspace=None, out=None, lse=None, stage: str = "all"):
+    """Dense paged decode; returns (out [B, s_q, h_q, dv] bf16, lse [B, s_q, h_q] fp32).
+
+    ``stage="split"`` runs only the split-KV kernel (then call
+    :func:`mla_combine` with the same workspace, out and lse)."""
     lib = _load()
+    fn = lib.mla_decode_paged if stage == "all" else lib.mla_splitkv_paged
     _need(q.dim() == 4 and kvcache.dim() == 4, "q is [B, s_q, h_q, d_qk], kvcache [blocks, 64, h_kv, d_qk]")
     _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
     _need(q.is_cuda and kvcache.is_cuda and block_table.is_cuda and cache_seqlens.is_cuda,
@@ -220,19 +230,23 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
     if softmax_scale is None:
         softmax_scale = d_qk ** -0.5
     out, lse, workspace, ws_bytes = _prep_outputs(q, meta, dv, workspace, out, lse)
-    rc = lib.mla_decode_paged(_ptr(q), _ptr(kvcache), _ptr(block_table), _ptr(cache_seqlens), B,
+    rc = fn(_ptr(q), _ptr(kvcache), _ptr(block_table), _ptr(cache_seqlens), B,
                               s_q, h_q, h_kv, d_qk, dv, nblk, page, block_table.shape[1],
                               1 if causal else 0, float(softmax_scale), _ptr(meta.meta_dev),
                               ctypes.byref(meta.info), _ptr(workspace), ws_bytes, _ptr(out),
                               _ptr(lse), _stream(q.device))
     _check(rc, "mla_decode_paged")
+    if stage == "split":
+        return out, lse, workspace
     return out, lse
 
 
 def mla_decode_sparse(q, kvcache, indices, dv: int, meta: Metadata,
-                      softmax_scale: float | None = None, workspace=None, out=None, lse=None):
+                      softmax_scale: float | None = None, workspace=None, out=None, lse=None,
+                      stage: str = "all"):
     """Top-k sparse decode; heads past the metadata's active count are not written."""
     lib = _load()
+    fn = lib.mla_decode_sparse if stage == "all" else lib.mla_splitkv_sparse
     _need(q.dim() == 4 and kvcache.dim() == 4 and indices.dim() == 3, "bad ranks")
     _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
     _need(indices.dtype == torch.int32, "indices must be int32")
@@ -249,11 +263,25 @@ def mla_decode_sparse(q, kvcache, indices, dv: int, meta: Metadata,
     if softmax_scale is None:
         softmax_scale = d_qk ** -0.5
     out, lse, workspace, ws_bytes = _prep_outputs(q, meta, dv, workspace, out, lse)
-    rc = lib.mla_decode_sparse(_ptr(q), _ptr(kvcache), _ptr(indices), B, s_q, h_q, h_kv, d_qk, dv,
+    rc = fn(_ptr(q), _ptr(kvcache), _ptr(indices), B, s_q, h_q, h_kv, d_qk, dv,
                                nblk, page, topk, float(softmax_scale), _ptr(meta.meta_dev),
                                ctypes.byref(meta.info), _ptr(workspace), ws_bytes, _ptr(out),
                                _ptr(lse), _stream(q.device))
     _check(rc, "mla_decode_sparse")
+    if stage == "split":
+        return out, lse, workspace
+    return out, lse
+
+
+def mla_combine(meta: Metadata, out, lse, workspace, dv: int = 512):
+    """LSE-merge the split partials in ``workspace`` into ``out``/``lse``."""
+    lib = _load()
+    B, s_q, h_q, _ = out.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.mla_combine(_ptr(meta.meta_dev), ctypes.byref(meta.info), B, s_q, h_q, dv,
+                         1 if meta.sparse else 0, _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                         _stream(out.device))
+    _check(rc, "mla_combine")
     return out, lse
 
 

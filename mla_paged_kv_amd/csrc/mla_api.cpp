@@ -65,36 +65,56 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
   return MLA_OK;
 }
 
-int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, void* workspace,
-           int32_t dv, void* stream) {
+enum { kStageSplit = 1, kStageCombine = 2 };
+
+void carve_workspace(const mla_sched_info* info, void* workspace, int32_t dv, float** ws_o,
+                     float** ws_lse) {
   const size_t o_bytes = size_t(info->total_slots) * info->rows * dv * sizeof(float);
-  kp.ws_o = static_cast<float*>(workspace);
-  kp.ws_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(o_bytes))
-                        : nullptr;
+  *ws_o = static_cast<float*>(workspace);
+  *ws_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(o_bytes))
+                      : nullptr;
+}
+
+int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, int32_t s_q,
+                         int32_t h_q, int32_t heads, bool sparse, void* workspace, int32_t dv,
+                         void* out, float* lse, hipStream_t st) {
+  if (info->num_split_units <= 0) return MLA_OK;
+  CombineParams cp;
+  float* ws_o;
+  float* ws_lse;
+  carve_workspace(info, workspace, dv, &ws_o, &ws_lse);
+  cp.meta = meta_dev;
+  cp.ws_o = ws_o;
+  cp.ws_lse = ws_lse;
+  cp.out = static_cast<uint16_t*>(out);
+  cp.lse = lse;
+  cp.off_num_splits = info->off_num_splits;
+  cp.off_split_list = info->off_split_list;
+  cp.num_split_units = info->num_split_units;
+  cp.rows = info->rows;
+  cp.s_q = s_q;
+  cp.h_q = h_q;
+  cp.heads = heads;
+  cp.sparse = sparse ? 1 : 0;
+  const hipError_t e = launch_combine(cp, st);
+  if (e != hipSuccess) return set_error(MLA_E_HIP, "combine launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, void* workspace,
+           int32_t dv, void* stream, int stages) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  carve_workspace(info, workspace, dv, &kp.ws_o, &kp.ws_lse);
   kp.num_parts = info->num_parts;
   kp.row_blocks = info->row_blocks;
   kp.rows = info->rows;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_splitkv(kp, d_qk, sparse, st);
-  if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
-  if (info->num_split_units > 0) {
-    CombineParams cp;
-    cp.meta = kp.meta;
-    cp.ws_o = kp.ws_o;
-    cp.ws_lse = kp.ws_lse;
-    cp.out = kp.out;
-    cp.lse = kp.lse;
-    cp.off_num_splits = info->off_num_splits;
-    cp.off_split_list = info->off_split_list;
-    cp.num_split_units = info->num_split_units;
-    cp.rows = info->rows;
-    cp.s_q = kp.s_q;
-    cp.h_q = kp.h_q;
-    cp.heads = kp.heads;
-    cp.sparse = sparse ? 1 : 0;
-    e = launch_combine(cp, st);
-    if (e != hipSuccess) return set_error(MLA_E_HIP, "combine launch: %s", hipGetErrorString(e));
+  if (stages & kStageSplit) {
+    const hipError_t e = launch_splitkv(kp, d_qk, sparse, st);
+    if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
+  if (stages & kStageCombine)
+    return launch_combine_stage(kp.meta, info, kp.s_q, kp.h_q, kp.heads, sparse, workspace, dv,
+                                kp.out, kp.lse, st);
   return MLA_OK;
 }
 
@@ -137,14 +157,17 @@ size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v) {
   return mla::align256(o) + mla::align256(l);
 }
 
-int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_table,
-                     const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
-                     int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
-                     int32_t page_block_size, int32_t bt_stride, int32_t causal,
-                     float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
-                     void* workspace, size_t workspace_bytes, void* out, float* lse,
-                     void* stream) {
-  using namespace mla;
+}  // extern "C"
+
+namespace mla {
+
+int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_table,
+                      const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                      int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                      int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                      float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      void* stream, int stages) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
                         meta_dev, info, workspace, workspace_bytes, out, lse);
@@ -179,16 +202,15 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
   kp.topk = 0;
   kp.causal = causal;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, false, workspace, dv, stream);
+  return launch(kp, info, d_qk, false, workspace, dv, stream, stages);
 }
 
-int mla_decode_sparse(const void* q, const void* kvcache, const int32_t* indices,
-                      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
-                      int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
-                      float softmax_scale, const int32_t* meta_dev,
-                      const mla_sched_info* info, void* workspace, size_t workspace_bytes,
-                      void* out, float* lse, void* stream) {
-  using namespace mla;
+int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indices,
+                       int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                       int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                       float softmax_scale, const int32_t* meta_dev,
+                       const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                       void* out, float* lse, void* stream, int stages) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
                         meta_dev, info, workspace, workspace_bytes, out, lse);
@@ -220,7 +242,82 @@ int mla_decode_sparse(const void* q, const void* kvcache, const int32_t* indices
   kp.topk = topk;
   kp.causal = 0;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, true, workspace, dv, stream);
+  return launch(kp, info, d_qk, true, workspace, dv, stream, stages);
+}
+
+}  // namespace mla
+
+extern "C" {
+
+#define MLA_PAGED_ARGS                                                                          \
+  const void *q, const void *kvcache, const int32_t *block_table, const int32_t *cache_seqlens, \
+      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,          \
+      int32_t num_blocks, int32_t page_block_size, int32_t bt_stride, int32_t causal,           \
+      float softmax_scale, const int32_t *meta_dev, const mla_sched_info *info,                 \
+      void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream
+#define MLA_PAGED_PASS                                                                          \
+  q, kvcache, block_table, cache_seqlens, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks,          \
+      page_block_size, bt_stride, causal, softmax_scale, meta_dev, info, workspace,             \
+      workspace_bytes, out, lse, stream
+#define MLA_SPARSE_ARGS                                                                         \
+  const void *q, const void *kvcache, const int32_t *indices, int32_t batch, int32_t s_q,      \
+      int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,                  \
+      int32_t page_block_size, int32_t topk, float softmax_scale, const int32_t *meta_dev,      \
+      const mla_sched_info *info, void *workspace, size_t workspace_bytes, void *out,           \
+      float *lse, void *stream
+#define MLA_SPARSE_PASS                                                                         \
+  q, kvcache, indices, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size, topk,     \
+      softmax_scale, meta_dev, info, workspace, workspace_bytes, out, lse, stream
+
+int mla_decode_paged(MLA_PAGED_ARGS) {
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine);
+}
+
+int mla_splitkv_paged(MLA_PAGED_ARGS) {
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit);
+}
+
+int mla_decode_sparse(MLA_SPARSE_ARGS) {
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine);
+}
+
+int mla_splitkv_sparse(MLA_SPARSE_ARGS) {
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit);
+}
+
+int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,
+                int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
+                size_t workspace_bytes, void* out, float* lse, void* stream) {
+  using namespace mla;
+  clear_error();
+  if (info == nullptr) return set_error(MLA_E_INVAL, "combine: null info");
+  if (batch < 0 || s_q < 1 || h_q < 1) return set_error(MLA_E_INVAL, "combine: bad shape");
+  if (dv != kDV) return set_error(MLA_E_NOTSUP, "combine: dv=%d (only 512)", dv);
+  if (sparse != 0 && sparse != 1) return set_error(MLA_E_INVAL, "combine: sparse=%d", sparse);
+  if (info->rows < 1 || info->total_slots < 0 || info->num_split_units < 0 ||
+      info->total_ints < kHeaderInts)
+    return set_error(MLA_E_INVAL, "combine: malformed metadata header");
+  int32_t heads;
+  if (sparse) {
+    if (int64_t(info->num_units) != int64_t(batch) * s_q)
+      return set_error(MLA_E_INVAL, "combine: metadata units %d != batch*s_q", info->num_units);
+    heads = info->rows;
+  } else {
+    if (info->num_units != batch || info->rows % s_q != 0)
+      return set_error(MLA_E_INVAL, "combine: metadata does not match batch/s_q");
+    heads = info->rows / s_q;
+  }
+  if (heads > h_q) return set_error(MLA_E_INVAL, "combine: metadata heads %d > h_q=%d", heads, h_q);
+  if (info->num_split_units == 0 || batch == 0) return MLA_OK;
+  if (!meta_dev || !out || !lse || !workspace)
+    return set_error(MLA_E_INVAL, "combine: null meta/out/lse/workspace");
+  if (!aligned(out, 16) || !aligned(lse, 4) || !aligned(workspace, 256))
+    return set_error(MLA_E_INVAL, "combine: misaligned out/lse/workspace");
+  if (workspace_bytes < mla_workspace_bytes(info, dv))
+    return set_error(MLA_E_NOSPC, "combine: workspace too small");
+  return launch_combine_stage(meta_dev, info, s_q, h_q, heads, sparse != 0,
+                              const_cast<void*>(workspace), dv, out, lse,
+                              static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

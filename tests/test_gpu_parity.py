@@ -192,6 +192,20 @@ def test_sparse_poisoned_invalid_rows_do_not_leak():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_stages_compose_to_decode():
+    import mla_paged_kv_amd as mla
+    case = make_dense_case(43, B=3, s_q=1, h_q=64, seqlens=[3000, 70, 900], spare_frac=0.1)
+    d = to_device(case)
+    meta = metadata(case, num_parts=9)
+    assert meta.num_split_units > 0
+    o1, l1 = run_gpu(d, meta)
+    out, lse, ws = mla.mla_decode_paged(d["q"], d["kvcache"], d["block_table"], d["cache_seqlens"],
+                                        512, meta, softmax_scale=case["softmax_scale"], stage="split")
+    mla.mla_combine(meta, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, out) and torch.equal(l1, lse)
+
+
 # ---------------------------------------------------------------- the five workloads at full size
 
 @pytest.mark.parametrize("k", [2, 3, 4, 5])
