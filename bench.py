@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512) on 1 GPU"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-KERNEL_SOURCES = ["mla_paged_kv_amd/csrc/mla_kernels.hip", "mla_paged_kv_amd/csrc/mla_kernels.h"]
+KERNEL_SOURCES = ["mla_paged_kv_amd/csrc/mla_splitkv.hip", "mla_paged_kv_amd/csrc/mla_kernels.h"]
 
 
 def kernel_hash() -> str:

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_sched.cpp", "mla_api.cpp", "mla_kernels.hip"]
+SOURCES = ["mla_sched.cpp", "mla_api.cpp", "mla_splitkv.hip", "mla_combine.hip"]
 
 # Packed-FP32 VALU ops are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
