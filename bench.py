@@ -19,8 +19,10 @@ Algorithmic work (what the method must do, not padded work):
           + block-table entries (or indices) read + sequence lengths.
 The split workspace traffic is overhead and is not counted.
 
-Prints one JSON line.  Per-kernel durations come from HIP events recorded on
-the stream the kernels run on, around each kernel of every timed step.
+Prints one JSON line.  The step time is the whole decode (split-KV then
+combine) timed back to back between HIP events; the per-kernel durations come
+from HIP events around runs of each kernel alone over the same number of
+launches, recorded on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -78,7 +80,7 @@ def algorithmic_work(case) -> dict:
                 keys=keys)
 
 
-def cpu_baseline(case, min_seconds: float, max_passes: int = 8) -> dict:
+def cpu_baseline(case, min_seconds: float, max_passes: int = 64) -> dict:
     """The FP64 oracle as it stands, on the host cores, over whole passes of
     the workload (at least one, until ``min_seconds`` have elapsed)."""
     import numpy as np  # noqa: F401
@@ -109,7 +111,23 @@ def cpu_baseline(case, min_seconds: float, max_passes: int = 8) -> dict:
                       f"(BLAS threads {cores}, host cpus {os.cpu_count()})"}
 
 
-def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600) -> dict:
+COPY_PROBE_BYTES = 256 << 20  # read once and written once by the copy probe
+
+
+def copy_probe(torch, dev, reps: int = 3):
+    """A plain copy of known size (COPY_PROBE_BYTES read, the same written),
+    run only under counter collection: its FETCH_SIZE / WRITE_SIZE readings
+    scale the counters of the decode kernels to bytes."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600,
+                   probe: bool = False) -> dict:
     import torch
 
     import mla_paged_kv_amd as mla
@@ -161,25 +179,35 @@ def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600) -> dic
         split(kvs[i % copies], meta)
         combine(meta)
     torch.cuda.synchronize()
+    if probe:
+        copy_probe(torch, dev)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # whole decode steps (split-KV then combine), back to back
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        a, b, c = ev[i]
-        a.record()
         split(kvs[i % copies], meta)
-        b.record()
         combine(meta)
-        c.record()
     stop.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / steps
-    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+
+    # each kernel alone over the same number of launches, between two events
+    # on the stream the kernels run on (torch's current stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for i in range(steps):
+        split(kvs[i % copies], meta)
+    ev[1].record()
+    ev[2].record()
+    for i in range(steps):
+        combine(meta)
+    ev[3].record()
+    torch.cuda.synchronize()
+    split_ms = ev[0].elapsed_time(ev[1]) / steps
+    comb_ms = ev[2].elapsed_time(ev[3]) / steps
 
     # rate with the scheduler and its upload inside every step
     torch.cuda.synchronize()
@@ -215,10 +243,14 @@ def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600) -> dic
     return res
 
 
-def load_traffic(k: int, steps_ms: float):
-    """HBM traffic per launch of the split-KV kernel from committed counter
-    summaries, if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"splitkv_traffic_workload{k}.json")
+def traffic_path(k: int) -> str:
+    return os.path.join(ROOT, "profiles", f"splitkv_traffic_workload{k}.json")
+
+
+def load_traffic(k: int):
+    """HBM bytes per launch of the split-KV kernel from the committed counter
+    summary of workload k, if it was taken on the current kernel source."""
+    path = traffic_path(k)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -226,6 +258,41 @@ def load_traffic(k: int, steps_ms: float):
     if d.get("kernel_hash") != kernel_hash():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def _counter_rows(path: str, counter: str):
+    import csv
+    rows = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def ingest_counters(k: int, fetch_csv: str, write_csv: str, command: str) -> dict:
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) of ``bench.py --workload k --copy-probe`` into HBM bytes per
+    split-KV launch.  Each counter is scaled by bytes / reading of the copy
+    probe in the same run (the neg kernel over COPY_PROBE_BYTES)."""
+    out = {"workload": k, "kernel_hash": kernel_hash(), "command": command}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(path, counter)
+        split = [v for n, v in rows if "mla_splitkv" in n]
+        probe = [v for n, v in rows if "neg_kernel" in n]
+        if not split or not probe:
+            raise SystemExit(f"{path}: no split-KV or copy-probe dispatches with {counter}")
+        kib = sum(split) / len(split)
+        probe_kib = sorted(probe)[len(probe) // 2]
+        factor = (COPY_PROBE_BYTES / 1024) / probe_kib
+        out[name] = {"counter": counter, "dispatches": len(split), "kib_per_launch": round(kib, 1),
+                     "probe_kib": round(probe_kib, 1), "probe_factor": round(factor, 4),
+                     "bytes_per_launch": int(kib * 1024 * factor)}
+    out["traffic_bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    with open(traffic_path(k), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
 
 
 def main():
@@ -239,7 +306,17 @@ def main():
                     help="extra workloads timed into 'other_workloads' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run the known-size copy used to scale HBM counters (profiling only)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two counter runs of --workload into the committed "
+                         "traffic summary and exit")
+    ap.add_argument("--ingest-command", default="", help="command recorded with --ingest-counters")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(args.workload, *args.ingest_counters, args.ingest_command)))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
@@ -251,10 +328,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    r = bench_workload(args.workload, args.steps, args.warmup)
+    r = bench_workload(args.workload, args.steps, args.warmup, probe=args.copy_probe)
     case = r["case"]
-    traffic = load_traffic(args.workload, r["split_ms"])
-    r["roofline"]["traffic"] = traffic
+    r["roofline"]["traffic"] = load_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),
@@ -290,6 +366,7 @@ def main():
         if k == args.workload:
             continue
         o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2))
+        o["roofline"]["traffic"] = load_traffic(k)
         others[str(k)] = {
             "workload": o["case"]["name"], "ms_per_step": round(o["ms_step"], 5),
             "tflops": round(o["tflops"], 2), "hbm_gbps": round(o["gbs"], 1),

@@ -1,11 +1,10 @@
 // LSE combine kernel of the paged MLA decode library, written for gfx950.
 //
 // mla_combine merges the fp32 partial outputs of a split unit by their base-2
-// log-sum-exps: one wavefront per (split unit, active row); lane k holds the
-// log-sum-exps of splits k, k+64, ... so up to 64 splits are reduced in one
-// pass of the wavefront and more in further passes (the DeepLink-org fork's
-// exact small-split combine path, widened to wave64), and the combine runs
-// over active rows only (the fork's active-head combine).
+// log-sum-exps, over active rows only (the DeepLink-org fork's active-head
+// combine).  Lane k of a wavefront holds the log-sum-exps of splits k, k+64,
+// ..., so up to 64 splits are merged in one pass (the fork's exact small-split
+// path, widened to wave64) and more in further passes.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -31,52 +30,73 @@ __device__ __forceinline__ unsigned short f2bf(float x) {
 
 }  // namespace
 
-// One wavefront per (split unit, row); lane k holds splits k, k+64, ...
+// One workgroup per (split unit, row).  Every wavefront derives the merged
+// log-sum-exp itself (lane k holds splits k, k+64, ...); the weighted sum of the
+// partial outputs is spread over the four wavefronts (wavefront w takes splits
+// w, w+4, ..., several loads in flight per lane) and reduced through LDS.
 __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
+  constexpr int kWaves = 4, kUnroll = 4;
+  __shared__ f32x4 red[kWaves - 1][64][2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int row_groups = (p.rows + 3) / 4;
-  const int k = blockIdx.x / row_groups;
-  const int row = (blockIdx.x - k * row_groups) * 4 + wave;
-  if (k >= p.num_split_units || row >= p.rows) return;
+  const int k = blockIdx.x / p.rows;
+  const int row = blockIdx.x - k * p.rows;
 
   const int32_t* meta = p.meta;
   const int u = meta[p.off_split_list + 2 * k];
   const int slot0 = meta[p.off_split_list + 2 * k + 1];
   const int nsplit = meta[p.off_num_splits + u + 1] - meta[p.off_num_splits + u];
+  const float* lse_col = p.ws_lse + size_t(slot0) * p.rows + row;  // split s at s * rows
 
-  // pass 1: max and sum of 2^lse over the splits
+  // merged LSE (base 2): max, then sum of 2^(lse - max)
   float mx = -__builtin_inff();
-  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, p.ws_lse[size_t(slot0 + s) * p.rows + row]);
+  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, lse_col[size_t(s) * p.rows]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   const float m_use = mx == -__builtin_inff() ? 0.f : mx;
   float sum = 0.f;
-  for (int s = lane; s < nsplit; s += 64)
-    sum += fast_exp2(p.ws_lse[size_t(slot0 + s) * p.rows + row] - m_use);
+  for (int s = lane; s < nsplit; s += 64) sum += fast_exp2(lse_col[size_t(s) * p.rows] - m_use);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
   const bool empty = !(sum > 0.f);
   const float lse2 = empty ? -__builtin_inff() : m_use + fast_log2(sum);
 
-  // pass 2: weighted sum of the partial outputs; lane owns columns 8*lane..+7
+  // weighted partial outputs; lane owns columns 8*lane .. 8*lane+7
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   if (!empty) {
-    for (int base = 0; base < nsplit; base += 64) {
-      const int s_l = base + lane;
-      const float w_l =
-          s_l < nsplit ? fast_exp2(p.ws_lse[size_t(slot0 + s_l) * p.rows + row] - lse2) : 0.f;
-      const int cnt = nsplit - base < 64 ? nsplit - base : 64;
-      for (int j = 0; j < cnt; ++j) {
-        const float w = __shfl(w_l, j);
-        const f32x4* src =
-            reinterpret_cast<const f32x4*>(p.ws_o + (size_t(slot0 + base + j) * p.rows + row) * kDV) +
-            2 * lane;
-        a0 += w * src[0];
-        a1 += w * src[1];
+    const float* o_col = p.ws_o + (size_t(slot0) * p.rows + row) * kDV + 8 * lane;
+    const size_t split_stride = size_t(p.rows) * kDV;
+    for (int s0 = wave; s0 < nsplit; s0 += kWaves * kUnroll) {
+      f32x4 v0[kUnroll], v1[kUnroll];
+      float w[kUnroll];
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int s = s0 + j * kWaves;
+        const bool ok = s < nsplit;
+        const float* src = o_col + size_t(ok ? s : s0) * split_stride;
+        v0[j] = *reinterpret_cast<const f32x4*>(src);
+        v1[j] = *reinterpret_cast<const f32x4*>(src + 4);
+        w[j] = ok ? fast_exp2(lse_col[size_t(ok ? s : s0) * p.rows] - lse2) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        a0 += w[j] * v0[j];
+        a1 += w[j] * v1[j];
       }
     }
   }
+  if (wave > 0) {
+    red[wave - 1][lane][0] = a0;
+    red[wave - 1][lane][1] = a1;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaves - 1; ++w) {
+    a0 += red[w][lane][0];
+    a1 += red[w][lane][1];
+  }
+
   int b, iq, h;
   if (p.sparse) {
     b = u / p.s_q;
@@ -98,8 +118,8 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  if (p.num_split_units <= 0) return hipSuccess;
-  const dim3 grid(p.num_split_units * ((p.rows + 3) / 4)), block(256);
+  if (p.num_split_units <= 0 || p.rows <= 0) return hipSuccess;
+  const dim3 grid(p.num_split_units * p.rows), block(256);
   hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);
   return hipGetLastError();
 }
