@@ -33,7 +33,7 @@ namespace {
 constexpr int32_t kPage = 64;
 constexpr int32_t kOverhead = 5;      // F, per-segment overhead in blocks
 constexpr int32_t kRowsPerGroup = 64; // query rows per workgroup
-constexpr int32_t kGroupsPerCU = 2;   // resident workgroups per compute unit
+constexpr int32_t kGroupsPerCU = 1;   // resident workgroups per compute unit (LDS-bound)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

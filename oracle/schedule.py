@@ -42,8 +42,9 @@ consecutive workspace slots, numbered over split units in unit order; an unsplit
 unit's single segment gets slot -1 (written straight to the output).
 
 Default part count: ``rows`` query rows per unit are processed 64 per
-workgroup, two workgroups per compute unit, so
-``P = max(1, (2 * num_cus) // ceil(rows / 64))``.
+workgroup and one workgroup is resident per compute unit (a workgroup holds
+two 64-token cache pages in LDS, 144 KiB of the 160 KiB), so that every part
+starts at once: ``P = max(1, num_cus // ceil(rows / 64))``.
 
 Metadata layout (int32):
 
@@ -63,7 +64,7 @@ import numpy as np
 PAGE_BLOCK = 64
 SPLIT_OVERHEAD_BLOCKS = 5
 ROWS_PER_WORKGROUP = 64
-WORKGROUPS_PER_CU = 2
+WORKGROUPS_PER_CU = 1
 HEADER_INTS = 16
 
 

@@ -50,11 +50,11 @@ def test_hand_worked_long_unit_even_cut():
 
 
 def test_default_part_count():
-    assert ref_num_parts(16, 256) == 512
-    assert ref_num_parts(64, 256) == 512
-    assert ref_num_parts(128, 256) == 256
-    assert ref_num_parts(256, 256) == 128
-    assert ref_num_parts(65, 256) == 256
+    assert ref_num_parts(16, 256) == 256
+    assert ref_num_parts(64, 256) == 256
+    assert ref_num_parts(128, 256) == 128
+    assert ref_num_parts(256, 256) == 64
+    assert ref_num_parts(65, 256) == 128
     assert ref_num_parts(10_000, 4) == 1
 
 
