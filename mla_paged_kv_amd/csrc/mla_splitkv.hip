@@ -1,23 +1,31 @@
 // Split-KV kernel of the paged MLA decode library, written for gfx950 (CDNA4).
 //
-// One workgroup = (part, row block) of the tile-scheduler metadata: 4
-// wavefronts, one per SIMD, each owning 16 query rows of the unit.  The
-// workgroup walks its part's segments (unit, block range, slot) as one stream
-// of 64-token tiles.  Each tile is gathered into LDS with direct global->LDS
-// loads -- a contiguous 64-row page reached through the block table for dense
-// decode, 64 scattered rows reached through the index list for sparse decode
-// -- into one of two buffers, so the next tile streams in while the current
-// one is computed:
+// One workgroup = (part, row block of 64 query rows) of the tile-scheduler
+// metadata: 4 wavefronts, one per SIMD.  The workgroup walks its part's
+// segments (unit, block range, slot) as one stream of 64-token tiles.  Each
+// tile is gathered into LDS with direct global->LDS loads -- a contiguous
+// 64-row page reached through the block table for dense decode, 64 scattered
+// rows reached through the index list for sparse decode -- into one of two
+// buffers, so the next tile streams in while the current one is computed:
 //
-//   S^T = K . Q^T      bf16 MFMA 16x16x32; K from LDS, Q^T resident in
-//                      registers for the whole segment
+//   S^T = K . Q^T      bf16 MFMA; K from LDS, Q^T resident in registers for
+//                      the whole segment
 //   online softmax     fp32, base 2, one query row per lane (reduced over the
-//                      4 lanes sharing it); the reference maximum is moved
-//                      only when it grows by more than 2^8, so the accumulator
-//                      is rarely rescaled (the result does not depend on it)
+//                      lanes sharing it); the reference maximum is moved only
+//                      when it grows by more than 2^8, so the accumulator is
+//                      rarely rescaled (the result does not depend on it)
 //   O^T += V^T . P^T   bf16 MFMA; P^T straight from registers, V^T read with
 //                      the LDS transpose read from the first 512 columns of
 //                      the same tile
+//
+// Two layouts of the four wavefronts:
+//  * pairs (more than 16 rows): wavefronts 2r and 2r+1 share query rows
+//    32r..32r+31.  Each computes S^T for its half of the tile's tokens over all
+//    d_qk and O^T for its half of the 512 value columns with 32x32x16 MFMAs;
+//    the two exchange their row maxima, row sums and bf16 P halves through
+//    LDS.  Every K and V element read from LDS then feeds 32 query rows.
+//  * single wavefronts (16 rows or fewer): each owns 16 rows and the whole
+//    tile with 16x16x32 MFMAs.
 //
 // The metadata of the tile after next (block-table entry and sequence length,
 // or the sparse index list) is fetched one step ahead, and the next segment's
@@ -32,12 +40,10 @@
 //
 // LDS tile layout: cache row t of a tile occupies 16-byte chunks
 // [t*CPR, (t+1)*CPR), with its chunk c stored at position c ^ f(t).  The
-// swizzle f spreads both operand reads over all banks: the 16 rows of one K
-// fragment read (one chunk column) and the 8 rows x 32 bytes of one V^T
-// transpose read land in distinct bank groups.  It is applied on the source
-// side of the global->LDS gather, and since f depends only on the low bits of
-// t, every operand address is one of a few per-lane bases plus a compile-time
-// offset.
+// swizzle f spreads both operand reads over all banks.  It is applied on the
+// source side of the global->LDS gather, and since f depends only on the low
+// bits of t, every operand address is one of a few per-lane bases plus a
+// compile-time offset.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -65,8 +71,12 @@ __device__ __forceinline__ cint* as_const(const int32_t* ptr) { return (cint*)(u
 constexpr int kPage = 64;       // tokens per tile (one page, or 64 sparse indices)
 constexpr int kWaves = 4;       // wavefronts per workgroup
 constexpr int kDV = 512;        // value width
+constexpr int kRowsPerGroup = 64;  // query rows per workgroup
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family parts:
+// a valid 32-bit data format, everything else zero.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -74,6 +84,11 @@ __device__ __forceinline__ unsigned short f2bf(float x) {
   return __builtin_bit_cast(unsigned short, (__bf16)x);
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and
+// scalar) accesses, not for the tile gathers still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 // Register-class pins: an empty asm statement that takes the value in an AGPR.
 // It emits no instruction; it keeps the long-lived accumulators and query
 // fragments in the accumulation registers, so the vector registers stay free
@@ -163,9 +178,16 @@ struct TileMeta {
 
 }  // namespace
 
-template <int D_QK, bool SPARSE, int RW>
+// PAIR = false: each wavefront owns 16 query rows and the whole tile (16x16x32
+// MFMAs).  PAIR = true: the two wavefronts of a pair share 32 query rows; each
+// computes S^T for its half of the tile's tokens over all d_qk and O^T for its
+// half of the 512 value columns (32x32x16 MFMAs), and the pair exchanges its
+// row maxima, row sums and bf16 P halves through LDS.  A pair reads each K and
+// V element from LDS once per 32 rows instead of once per 16.
+template <int D_QK, bool SPARSE, bool PAIR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_splitkv(SplitKVParams p) {
+  constexpr int RW = PAIR ? 32 : 16;  // query rows per wavefront (pair)
   using S = Shape<RW>;
   using C = typename S::C;
   constexpr int CPR = D_QK / 8;    // 16-byte chunks per cache row
@@ -179,15 +201,22 @@ void mla_splitkv(SplitKVParams p) {
   constexpr int FMAX = CPR == 72 ? 8 : 16;  // swizzle values are below this
   constexpr int NKB = FMAX / CK;   // K-read bases (kk mod NKB)
   constexpr int NVB = FMAX / CV;   // V-read bases (ct mod NVB)
-  constexpr int NCT = S::NCT;
+  constexpr int NCT = PAIR ? S::NCT / 2 : S::NCT;  // output column tiles per wavefront
+  constexpr int NX = PAIR ? kWaves : 1;             // pair exchange slots
   static_assert(NLD % kWaves == 0, "whole load instructions per wave");
+  static_assert(S::NV == 16 || PAIR, "16 scores per lane");
   __shared__ __attribute__((aligned(1024))) uint8_t buf_a[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf_b[BUF];
   __shared__ __attribute__((aligned(16))) uint32_t l2_sink[kWaves * 64];  // written, never read
+  __shared__ __attribute__((aligned(16))) s16x8 x_p[NX][2][64];  // bf16 P of a pair half
+  __shared__ float x_max[NX][32];                                 // row maxima of a half
+  __shared__ float x_sum[NX][32];                                 // row sums of a half
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int lrow = lane % RW;  // query row owned within the wave
+  const int rgrp = PAIR ? wave >> 1 : wave;  // row group of the wavefront
+  const int half = PAIR ? wave & 1 : 0;      // pair half: token half and column half
+  const int lrow = lane % RW;  // query row owned within the row group
   const int lgrp = lane / RW;  // k-group of the MFMA operands
 
   const int total = p.num_parts * p.row_blocks;
@@ -205,7 +234,7 @@ void mla_splitkv(SplitKVParams p) {
   auto seg_b1 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 2]; };
   auto seg_slot = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 3]; };
 
-  const int row0 = rb * (kWaves * RW) + wave * RW;
+  const int row0 = rb * kRowsPerGroup + rgrp * RW;
   const bool wave_active = row0 < p.rows;
   const int row = row0 + lrow;
   const bool row_ok = row < p.rows;
@@ -225,7 +254,7 @@ void mla_splitkv(SplitKVParams p) {
     const int fk = S::template swz<CPR>(lrow);
 #pragma unroll
     for (int j = 0; j < NKB; ++j)
-      kbase[j] = lrow * RSB + 16 * (lgrp ^ (fk % CK)) + 16 * CK * ((j ^ (fk / CK)) - j);
+      kbase[j] = (32 * half + lrow) * RSB + 16 * (lgrp ^ (fk % CK)) + 16 * CK * ((j ^ (fk / CK)) - j);
     const int y = S::vchunk(0, lane);
 #pragma unroll
     for (int h = 0; h < NVH; ++h) {
@@ -233,7 +262,8 @@ void mla_splitkv(SplitKVParams p) {
       const int fv = S::template swz<CPR>(vr);
 #pragma unroll
       for (int j = 0; j < NVB; ++j)
-        vbase[h][j] = vr * RSB + 16 * (y ^ (fv % CV)) + 16 * CV * ((j ^ (fv / CV)) - j) + 8 * (lane & 1);
+        vbase[h][j] = vr * RSB + 16 * (y ^ (fv % CV)) + 16 * CV * ((j ^ (fv / CV)) - j) + 8 * (lane & 1) +
+                      16 * CV * NCT * half;
     }
   }
 
@@ -273,6 +303,16 @@ void mla_splitkv(SplitKVParams p) {
     return m;
   };
 
+  // Buffer resource of one physical page (dense decode).  Page gathers and
+  // warm-ups use buffer loads: unlike global (flat-encoded) loads into LDS,
+  // they leave the LDS wait counter to LDS reads, so the operand waits of the
+  // tile being computed stay exact while the next tile streams in.
+  auto page_rsrc = [&](int phys) __attribute__((always_inline)) {
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>(p.kv) + size_t(phys) * kPage * D_QK * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, kPage * D_QK * 2,
+                                            kBufferWord3);
+  };
+
   // ---- tile gather into `dst`; returns the sparse validity mask ----
   // Every lane of every load fetches an in-bounds row: the tail of a
   // request's last page repeats its last cached token (masked out of the
@@ -284,6 +324,7 @@ void mla_splitkv(SplitKVParams p) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(p.kv);
     int tmax = kPage - 1;
     int idx_lane = 0;
+    const __amdgpu_buffer_rsrc_t page = page_rsrc(SPARSE ? 0 : m.phys);  // dense only
     if constexpr (SPARSE) {
       const bool ok = m.idx >= 0 && m.idx < p.num_rows;
       vmask = __ballot(ok);
@@ -291,7 +332,6 @@ void mla_splitkv(SplitKVParams p) {
       const int sub = __shfl(m.idx, __builtin_ctzll(vmask));
       idx_lane = ok ? m.idx : sub;
     } else {
-      base += size_t(m.phys) * kPage * D_QK * 2;
       const int vt = m.len - blk * kPage;
       tmax = vt < 1 ? 0 : (vt > kPage ? kPage - 1 : vt - 1);
     }
@@ -299,19 +339,23 @@ void mla_splitkv(SplitKVParams p) {
     // q % CPR, i.e. source chunk (q % CPR) ^ f(t); successive loads of a wave
     // are 64 * kWaves = 256 chunks apart
     constexpr int kStep = 64 * kWaves;
-    int t = (wave * 64 + lane) / CPR;
-    int c = (wave * 64 + lane) - t * CPR;
+    // recomputed per tile from an opaque copy of the thread id, so the
+    // compiler does not keep 18 per-lane source offsets alive across the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    int t = tid / CPR;
+    int c = tid - t * CPR;
 #pragma unroll
     for (int i = 0; i < NLD / kWaves; ++i) {
       const int n = wave + i * kWaves;
       const int cc = c ^ S::template swz<CPR>(t);
-      const uint8_t* src;
       if constexpr (SPARSE) {
-        src = base + size_t(__shfl(idx_lane, t)) * D_QK * 2 + cc * 16;
+        const uint8_t* src = base + size_t(__shfl(idx_lane, t)) * D_QK * 2 + cc * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + n * 1024), 16, 0, 0);
       } else {
-        src = base + (t < tmax ? t : tmax) * (D_QK * 2) + cc * 16;
+        const int off = (t < tmax ? t : tmax) * (D_QK * 2) + cc * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(page, (lds_void*)(dst + n * 1024), 16, off, 0, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + n * 1024), 16, 0, 0);
       t += kStep / CPR;
       c += kStep % CPR;
       if (c >= CPR) {
@@ -339,18 +383,22 @@ void mla_splitkv(SplitKVParams p) {
       for (int k = wave; k < kRowLines; k += kWaves)
         __builtin_amdgcn_global_load_lds(row_ptr + k * kLine, dst, 4, 0, 0);
     } else {
-      const uint8_t* page = kv + size_t(m.phys) * kPage * D_QK * 2;
+      const __amdgpu_buffer_rsrc_t page = page_rsrc(m.phys);
       constexpr int kLines = kPage * kRowLines;
 #pragma unroll
       for (int k = 0; k < (kLines + 255) / 256; ++k) {
         const int line = k * 256 + wave * 64 + lane;
         if (k * 256 + wave * 64 < kLines)
-          __builtin_amdgcn_global_load_lds(page + line * kLine, dst, 4, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(page, dst, 4, line * kLine, 0, 0, 0);
       }
     }
   };
 
   // ---- per-segment state ----
+  // m_run: reference maximum (base 2) of the lane's row, identical in both
+  // halves of a pair.  l_part: sum of the softmax numerators; per lane for
+  // 16-row wavefronts (reduced over the row's lanes at the end), the row total
+  // for pairs.
   bf16x8 qf[KK];
   C acc[NCT];
   float m_run = -__builtin_inff();
@@ -363,7 +411,7 @@ void mla_splitkv(SplitKVParams p) {
     const uint16_t* qp = p.q + row_index(u, row_ok ? row : p.rows - 1) * D_QK + 8 * lgrp;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * S::KD);
-    if constexpr (RW == 16) {  // with 16 rows per wave the queries fit beside acc
+    if constexpr (!PAIR) {  // with 16 rows per wave the queries fit beside acc
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) pin_agpr(qf[kk]);
     }
@@ -378,26 +426,29 @@ void mla_splitkv(SplitKVParams p) {
     l_part = 0.f;
   };
 
-  // reduction over the lanes that share a query row
+  // reduction over the lanes of one wavefront that share a query row
   auto row_sum = [&](float x) __attribute__((always_inline)) {
-    if constexpr (RW == 16) x += __shfl_xor(x, 16);
+    if constexpr (!PAIR) x += __shfl_xor(x, 16);
     return x + __shfl_xor(x, 32);
   };
   auto row_max = [&](float x) __attribute__((always_inline)) {
-    if constexpr (RW == 16) x = fmaxf(x, __shfl_xor(x, 16));
+    if constexpr (!PAIR) x = fmaxf(x, __shfl_xor(x, 16));
     return fmaxf(x, __shfl_xor(x, 32));
   };
 
-  // Writes the segment result of this lane's row; a segment without tokens
-  // (empty_seg) writes O = 0 and LSE = -inf.
+  // Writes the segment result of this lane's row (a pair half writes its own
+  // value columns); a segment without tokens (empty_seg) writes O = 0 and
+  // LSE = -inf.
   auto write_segment = [&](size_t orow, int slot, bool empty_seg) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);
-    const float l_tot = empty_seg ? 0.f : row_sum(l_part);
+    const float l_tot = empty_seg ? 0.f : (PAIR ? l_part : row_sum(l_part));
     const bool empty = !(l_tot > 0.f) || seg_first;
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse2 = empty ? -__builtin_inff() : m_run + fast_log2(l_tot);
     if (!row_ok) return;
+    const int ct0 = NCT * half;  // first value column tile of this wavefront
+    const bool lse_lane = lgrp == 0 && half == 0;
     if (slot < 0) {
       uint16_t* o = p.out + orow * kDV;
 #pragma unroll
@@ -409,10 +460,11 @@ void mla_splitkv(SplitKVParams p) {
           for (int e = 0; e < 4; ++e) v[e] = empty ? 0.f : acc[ct][j + e] * inv;
           const uint32_t lo = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
           const uint32_t hi = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
-          *reinterpret_cast<uint2*>(o + S::col(ct, j, lgrp)) = uint2{lo, hi};
+          *reinterpret_cast<uint2*>(o + S::col(ct0 + ct, j, lgrp)) = uint2{lo, hi};
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (lgrp == 0) p.lse[orow] = lse2 * kLn2;
+      if (lse_lane) p.lse[orow] = lse2 * kLn2;
     } else {
       const size_t wrow = size_t(slot) * p.rows + row;
       float* o = p.ws_o + wrow * kDV;
@@ -423,10 +475,11 @@ void mla_splitkv(SplitKVParams p) {
           f32x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = empty ? 0.f : acc[ct][j + e] * inv;
-          *reinterpret_cast<f32x4*>(o + S::col(ct, j, lgrp)) = v;
+          *reinterpret_cast<f32x4*>(o + S::col(ct0 + ct, j, lgrp)) = v;
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (lgrp == 0) p.ws_lse[wrow] = lse2;
+      if (lse_lane) p.ws_lse[wrow] = lse2;
     }
   };
 
@@ -435,32 +488,45 @@ void mla_splitkv(SplitKVParams p) {
   // queries are loaded once the QK product no longer needs the current ones.
   auto compute_tile = [&](const uint8_t* buf, int blk, uint64_t vmask,
                           int next_q_unit) __attribute__((always_inline)) {
-    constexpr int QD = RW == 16 ? 2 : 1;  // K fragments prefetched this many k-steps ahead
-    C st[S::TT];
-#pragma unroll
-    for (int tt = 0; tt < S::TT; ++tt) st[tt] = C{};
-    bf16x8 kf[QD + 1][S::TT];
+    // S^T accumulators: 16-row wavefronts hold TT token tiles of 16; a pair
+    // half holds its 32 tokens as two accumulation chains (even and odd
+    // k-steps) that are added at the end.
+    constexpr int NST = PAIR ? 2 : S::TT;
+    constexpr int QD = PAIR ? 4 : 2;  // K fragments prefetched this many k-steps ahead
+    constexpr int NTT = PAIR ? 1 : S::TT;  // token tiles read per k-step
+    C st[NST];
+    bf16x8 kf[QD + 1][NTT];
     auto load_k = [&](int kk) __attribute__((always_inline)) {
       const uint8_t* kb = buf + kbase[kk % NKB];
 #pragma unroll
-      for (int tt = 0; tt < S::TT; ++tt)
+      for (int tt = 0; tt < NTT; ++tt)
         kf[kk % (QD + 1)][tt] =
             *reinterpret_cast<const bf16x8*>(kb + tt * S::TW * RSB + kk * 16 * CK);
     };
 #pragma unroll
-    for (int kk = 0; kk < QD; ++kk) load_k(kk);
+    for (int kk = 0; kk < QD; ++kk) {
+      load_k(kk);
+      __builtin_amdgcn_sched_barrier(0);  // keep the ring in k-step order
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + QD < KK) load_k(kk + QD);
+      if constexpr (PAIR) {
+        const int c = kk & 1;
+        st[c] = S::mfma(kf[kk % (QD + 1)][0], qf[kk], kk < 2 ? C{} : st[c]);
+      } else {
 #pragma unroll
-      for (int tt = 0; tt < S::TT; ++tt) st[tt] = S::mfma(kf[kk % (QD + 1)][tt], qf[kk], st[tt]);
+        for (int tt = 0; tt < NTT; ++tt)
+          st[tt] = S::mfma(kf[kk % (QD + 1)][tt], qf[kk], kk == 0 ? C{} : st[tt]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (PAIR) st[0] += st[1];
     if (next_q_unit >= 0) load_q(next_q_unit);
 
     // V^T fragments, prefetched PD (k-step, column-tile) steps ahead; the
     // first PD are issued before the softmax so their latency hides behind it
-    constexpr int PD = RW == 16 ? 8 : 3;
+    constexpr int PD = PAIR ? 6 : 8;
     constexpr int NSTEP = S::KC * NCT;
     s16x4 vf[PD + 1][2];
     auto load_v = [&](int i) __attribute__((always_inline)) {
@@ -473,48 +539,87 @@ void mla_splitkv(SplitKVParams p) {
       }
     };
 #pragma unroll
-    for (int i = 0; i < PD; ++i) load_v(i);
+    for (int i = 0; i < PD; ++i) {
+      load_v(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // mask + online softmax (base 2), scores in place
+    // mask + online softmax (base 2), 16 scores per lane, in place
+    auto score = [&](int v) __attribute__((always_inline)) -> float {
+      if constexpr (PAIR) return st[0][v];
+      else return st[v / S::CREG][v % S::CREG];
+    };
+    auto set_score = [&](int v, float x) __attribute__((always_inline)) {
+      if constexpr (PAIR) st[0][v] = x;
+      else st[v / S::CREG][v % S::CREG] = x;
+    };
     float mloc = -__builtin_inff();
 #pragma unroll
-    for (int v = 0; v < S::NV; ++v) {
-      const int t = S::tok(v, lgrp);
+    for (int v = 0; v < 16; ++v) {
+      const int t = 32 * half + S::tok(v, lgrp);
       bool vis;
       if constexpr (SPARSE) {
         vis = (vmask >> t) & 1;
       } else {
         vis = blk * kPage + t < n_vis;
       }
-      const float x = vis ? st[v / S::CREG][v % S::CREG] * p.scale_log2 : -__builtin_inff();
-      st[v / S::CREG][v % S::CREG] = x;
+      const float x = vis ? score(v) * p.scale_log2 : -__builtin_inff();
+      set_score(v, x);
       mloc = fmaxf(mloc, x);
     }
     mloc = row_max(mloc);
+    if constexpr (PAIR) {  // maximum over both token halves
+      if (lane < 32) x_max[wave][lane] = mloc;
+      lds_barrier();
+      mloc = fmaxf(mloc, x_max[wave ^ 1][lane & 31]);
+    }
     const bool grow = mloc > m_run + kRescaleSlack;
-    if (__any(grow)) {
+    const bool rescale = __any(grow);
+    if (rescale) {
       const float m_new = grow ? mloc : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
       m_run = m_new;
       l_part *= alpha;
       if (!seg_first) {
+        // one column tile at a time, each back in its AGPRs before the next
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[ct] *= alpha;
+        for (int ct = 0; ct < NCT; ++ct) {
+          pin_agpr(acc[ct]);  // read out of the AGPRs here, not earlier
+          acc[ct] *= alpha;
+          pin_agpr(acc[ct]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);
     const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
     float psum = 0.f;
-    s16x8 pk[S::KC];  // P^T operand of PV k-step kc: scores 8kc .. 8kc+7
+    s16x8 pk[2];  // this lane's P^T operand: scores 8c .. 8c+7
 #pragma unroll
-    for (int v = 0; v < S::NV; ++v) {
-      const float pe = fast_exp2(st[v / S::CREG][v % S::CREG] - m_use);
+    for (int v = 0; v < 16; ++v) {
+      const float pe = fast_exp2(score(v) - m_use);
       psum += pe;
       pk[v >> 3][v & 7] = (short)f2bf(pe);
     }
-    l_part += psum;
+    s16x8 pp[2];  // the partner half's P^T operand (pairs)
+    if constexpr (PAIR) {
+      const float own = row_sum(psum);
+      x_p[wave][0][lane] = pk[0];
+      x_p[wave][1][lane] = pk[1];
+      if (lane < 32) x_sum[wave][lane] = own;
+      lds_barrier();
+      pp[0] = x_p[wave ^ 1][0][lane];
+      pp[1] = x_p[wave ^ 1][1][lane];
+      const float other = x_sum[wave ^ 1][lane & 31];
+      l_part += half == 0 ? own + other : other + own;  // same sum in both halves
+    } else {
+      l_part += psum;
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T; a pair's PV k-steps 0,1 cover tokens 0..31 (half 0's
+    // scores) and 2,3 tokens 32..63 (half 1's)
     auto pv = [&](bool from_zero) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < NSTEP; ++i) {
@@ -522,8 +627,11 @@ void mla_splitkv(SplitKVParams p) {
         const int kc = i / NCT, ct = i % NCT;
         const s16x4 lo = vf[i % (PD + 1)][0], hi = vf[i % (PD + 1)][1];
         const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        s16x8 pb;
+        if constexpr (PAIR) pb = (kc >> 1) == half ? pk[kc & 1] : pp[kc & 1];
+        else pb = pk[kc];
         const C c_in = (from_zero && kc == 0) ? C{} : acc[ct];
-        acc[ct] = S::mfma(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pk[kc]), c_in);
+        acc[ct] = S::mfma(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pb), c_in);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -570,7 +678,10 @@ void mla_splitkv(SplitKVParams p) {
     cmask = load_tile(buf_a, cblk, m0);
   }
   // tiles j+1 (gathered at the next step) and j+2 (warmed into L2 at the next
-  // step); the metadata of tile j+3 is fetched during the step
+  // step); the metadata of tile j+3 is read at the end of the step.  All
+  // scalar metadata reads of a step happen after its compute: a scalar load in
+  // flight shares the LDS wait counter and would turn every LDS operand wait of
+  // the tile into a full drain.
   int ns, nblk, n2s, n2blk;
   advance(cs, cblk, ns, nblk);
   TileMeta nmeta{0, 0, -1}, n2meta{0, 0, -1};
@@ -582,26 +693,23 @@ void mla_splitkv(SplitKVParams p) {
     if (n2s < seg_end) n2meta = fetch_meta(n2s, n2blk);
     warm_tile(nmeta);
   }
+  // the current tile ends its segment / the unit whose queries follow it
+  bool seg_last = cblk + 1 >= seg_b1(cs);
+  int next_q_unit = (seg_last && ns < seg_end) ? seg_u(ns) : -1;
 
   // One step computes the tile in `cur_buf` while the next one streams into
   // `nxt_buf`.  The two buffers are distinct LDS objects named statically at
   // every call site, so the compiler can tell reads of one from the
   // asynchronous writes into the other and does not wait for those writes.
   auto step = [&](const uint8_t* cur_buf, uint8_t* nxt_buf) __attribute__((always_inline)) -> bool {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);  // loop-carried in AGPRs
     wait_vmem();
     __syncthreads();
     uint64_t nmask = 0;
-    int n3s = seg_end, n3blk = 0;
-    TileMeta n3meta{0, 0, -1};
     if (ns < seg_end) nmask = load_tile(nxt_buf, nblk, nmeta);
-    if (n2s < seg_end) {
-      warm_tile(n2meta);
-      advance(n2s, n2blk, n3s, n3blk);
-      if (n3s < seg_end) n3meta = fetch_meta(n3s, n3blk);
-    }
-    const bool seg_last = cblk + 1 >= seg_b1(cs);
-    const int next_q_unit = (seg_last && ns < seg_end) ? seg_u(ns) : -1;
-    if (wave_active) {
+    if (n2s < seg_end) warm_tile(n2meta);
+    if (PAIR || wave_active) {  // a pair's exchange barriers need all four wavefronts
       if (!SPARSE || cmask != 0) {
         compute_tile(cur_buf, cblk, cmask, next_q_unit);
       } else if (next_q_unit >= 0) {
@@ -621,6 +729,12 @@ void mla_splitkv(SplitKVParams p) {
       }
     }
     if (ns >= seg_end) return false;
+    int n3s = seg_end, n3blk = 0;
+    TileMeta n3meta{0, 0, -1};
+    if (n2s < seg_end) {
+      advance(n2s, n2blk, n3s, n3blk);
+      if (n3s < seg_end) n3meta = fetch_meta(n3s, n3blk);
+    }
     cs = ns;
     cblk = nblk;
     cmask = nmask;
@@ -630,6 +744,8 @@ void mla_splitkv(SplitKVParams p) {
     n2s = n3s;
     n2blk = n3blk;
     n2meta = n3meta;
+    seg_last = cblk + 1 >= seg_b1(cs);
+    next_q_unit = (seg_last && ns < seg_end) ? seg_u(ns) : -1;
     return true;
   };
   for (;;) {
@@ -642,17 +758,20 @@ hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, hipStre
   const int groups = p.num_parts * p.row_blocks;
   if (groups <= 0) return hipSuccess;
   const dim3 grid(groups), block(256);
+  const bool pair = true;
+#define MLA_LAUNCH(D, SP)                                                             \
+  do {                                                                                \
+    if (pair)                                                                         \
+      hipLaunchKernelGGL((mla_splitkv<D, SP, true>), grid, block, 0, stream, p);      \
+    else                                                                              \
+      hipLaunchKernelGGL((mla_splitkv<D, SP, false>), grid, block, 0, stream, p);     \
+  } while (0)
   if (d_qk == 576) {
-    if (sparse)
-      hipLaunchKernelGGL((mla_splitkv<576, true, 16>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((mla_splitkv<576, false, 16>), grid, block, 0, stream, p);
+    if (sparse) MLA_LAUNCH(576, true); else MLA_LAUNCH(576, false);
   } else {
-    if (sparse)
-      hipLaunchKernelGGL((mla_splitkv<512, true, 16>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((mla_splitkv<512, false, 16>), grid, block, 0, stream, p);
+    if (sparse) MLA_LAUNCH(512, true); else MLA_LAUNCH(512, false);
   }
+#undef MLA_LAUNCH
   return hipGetLastError();
 }
 
