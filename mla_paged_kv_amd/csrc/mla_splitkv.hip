@@ -87,6 +87,28 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Reductions over lanes l and l ^ 32 (the two k-groups that share a query
+// row) with v_permlane32_swap, which exchanges the upper 32 lanes of its
+// first operand with the lower 32 lanes of its second: swapping a value with
+// a copy of itself leaves its lower half broadcast in one register and its
+// upper half in the other.  It is written out (with the wait states the
+// instruction needs after a VALU write of its operands) because the compiler
+// folds the builtin's two results into one when both operands are equal.
+__device__ __forceinline__ void swap_halves(float v, float& lo, float& hi) {
+  lo = v;
+  hi = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  float lo, hi;
+  swap_halves(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  float lo, hi;
+  swap_halves(v, lo, hi);
+  return lo + hi;
+}
 // Register-class pin: an empty asm statement that takes the value in AGPRs.
 // It emits no instruction; it keeps the long-lived accumulators in the
 // accumulation registers, so the vector registers stay free for the per-tile
@@ -168,7 +190,7 @@ void mla_splitkv(SplitKVParams p) {
   constexpr int kLines = kPage * D_QK * 2 / 128;     // 128-byte lines of a page
   constexpr int NWARM = (kLines + 255) / 256;       // warm-up loads per wavefront
   static_assert(NLD % kWaves == 0 && (16 * CPR) % 64 == 0, "16 whole rows per wavefront");
-  static_assert(2 * NLW <= KK && 8 * NWARM <= NSTEP, "gather slices fit the MFMA loops");
+  static_assert(NLW <= 2 * KK && NWARM <= NSTEP, "gather slices fit the MFMA loops");
   __shared__ __attribute__((aligned(1024))) uint8_t buf_a[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf_b[BUF];
   __shared__ __attribute__((aligned(16))) uint32_t l2_sink[kWaves * 64];  // written, never read
@@ -458,7 +480,10 @@ void mla_splitkv(SplitKVParams p) {
       if (kk + QD < KK) load_k(kk + QD);
       const int c = kk & 1;
       st[c] = mfma(kf[kk % (QD + 1)], qf[kk], kk < 2 ? f32x16{} : st[c]);
-      if (c == 0 && kk / 2 < NLW) gather_slice(kk / 2);
+      // the next tile's gather goes out early (two slices per k-step) so it
+      // has the rest of the tile to arrive
+      if (2 * kk < NLW) gather_slice(2 * kk);
+      if (2 * kk + 1 < NLW) gather_slice(2 * kk + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     st[0] += st[1];
@@ -509,7 +534,7 @@ void mla_splitkv(SplitKVParams p) {
         mloc = fmaxf(mloc, x);
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = xor32_max(mloc);
     if (lane < 32) x_max[wave][lane] = mloc;  // maximum over both token halves
     lds_barrier();
     mloc = fmaxf(mloc, x_max[wave ^ 1][lane & 31]) * p.scale_log2;
@@ -542,7 +567,7 @@ void mla_splitkv(SplitKVParams p) {
       pk[v >> 3][v & 7] = (short)f2bf(pe);
     }
     // exchange P halves and row sums with the pair partner
-    const float own = psum + __shfl_xor(psum, 32);
+    const float own = xor32_sum(psum);
     x_p[wave][0][lane] = pk[0];
     x_p[wave][1][lane] = pk[1];
     if (lane < 32) x_sum[wave][lane] = own;
@@ -566,7 +591,7 @@ void mla_splitkv(SplitKVParams p) {
         const s16x8 pb = (kc >> 1) == half ? pk[kc & 1] : pp[kc & 1];
         const f32x16 c_in = (from_zero && kc == 0) ? f32x16{} : acc[ct];
         acc[ct] = mfma(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pb), c_in);
-        if (i % 8 == 0 && i / 8 < NWARM) warm_slice(i / 8);
+        if (i < NWARM) warm_slice(i);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
