@@ -170,7 +170,9 @@ struct Gather {
 
 }  // namespace
 
-template <int D_QK, bool SPARSE>
+// WIDE (sparse only): the cache pool is 4 GiB or larger, so rows are reached
+// with 64-bit addresses instead of 32-bit offsets into one buffer resource.
+template <int D_QK, bool SPARSE, bool WIDE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_splitkv(SplitKVParams p) {
   // The body is compiled for the GPU only; the host pass needs just the
@@ -299,6 +301,11 @@ void mla_splitkv(SplitKVParams p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, kPage * D_QK * 2,
                                             kBufferWord3);
   };
+  // the whole pool (sparse rows, pools below 4 GiB)
+  auto pool_rsrc = [&]() __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), 0,
+                                            int(uint32_t(p.num_rows) * uint32_t(RSB)), kBufferWord3);
+  };
   auto plan_gather = [&](int blk, const TileMeta& m) __attribute__((always_inline)) -> Gather {
     Gather g;
     g.phys = SPARSE ? 0 : m.phys;
@@ -331,10 +338,17 @@ void mla_splitkv(SplitKVParams p) {
     lds_void* to = (lds_void*)(dst + n * 1024);
     const int t = 16 * wave + tl + (second ? 1 : 0);  // tile row of this lane
     if constexpr (SPARSE) {
-      const int r = __shfl(g.idx, t);
+      // the load covers two tile rows, so two uniform index reads suffice
+      const int r0 = __builtin_amdgcn_readlane(g.idx, 16 * wave + tl);
+      const int r1 = bnd < 64 ? __builtin_amdgcn_readlane(g.idx, 16 * wave + tl + 1) : r0;
+      const int r = second ? r1 : r0;
       const int in_row = ((q0 + ln) * 16 - (tl + (second ? 1 : 0)) * RSB) ^ f16;
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * RSB + in_row;
-      __builtin_amdgcn_global_load_lds(src, to, 16, 0, 0);
+      if constexpr (WIDE) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * RSB + in_row;
+        __builtin_amdgcn_global_load_lds(src, to, 16, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), to, 16, r * RSB + in_row, 0, 0, 0);
+      }
     } else {
       // in-page offset of source chunk q ^ f(t), moved down to row tmax for
       // rows past it
@@ -352,23 +366,26 @@ void mla_splitkv(SplitKVParams p) {
   // One dword of every 128-byte line of the tile is loaded into a scratch LDS
   // slot that is never read: the lines are then in L2 when the tile's gather
   // is issued one step later, so that gather waits for L2 instead of HBM and
-  // two tiles' worth of HBM reads are in flight per workgroup.
+  // two tiles' worth of HBM reads are in flight per workgroup.  The warm-up is
+  // issued first in a step, so it has a whole step to complete before the
+  // next step's wait for the gather issued after it.
   auto warm_one = [&](const TileMeta& m, int k) __attribute__((always_inline)) {
     lds_void* dst = (lds_void*)(l2_sink + wave * 64);
     if constexpr (SPARSE) {
       constexpr int kRowLines = D_QK * 2 / 128;
-      const int line = wave + kWaves * k;
-      if (line < kRowLines) {
-        const bool ok = m.idx >= 0 && m.idx < p.num_rows;
-        const uint8_t* row_ptr =
-            reinterpret_cast<const uint8_t*>(p.kv) + size_t(ok ? m.idx : 0) * RSB;
+      const int line = min(wave + kWaves * k, kRowLines - 1);
+      const bool ok = m.idx >= 0 && m.idx < p.num_rows;
+      const int r = ok ? m.idx : 0;
+      if constexpr (WIDE) {
+        const uint8_t* row_ptr = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * RSB;
         __builtin_amdgcn_global_load_lds(row_ptr + line * 128, dst, 4, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), dst, 4, r * RSB + line * 128, 0, 0, 0);
       }
     } else {
-      const int first = 64 * (wave + kWaves * k);  // uniform
-      if (first < kLines)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(m.phys), dst, 4, (first + lane) * 128, 0,
-                                                0, 0);
+      const int first = min(64 * (wave + kWaves * k), kLines - 64);  // uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(m.phys), dst, 4, (first + lane) * 128, 0, 0,
+                                              0);
     }
   };
 
@@ -458,8 +475,8 @@ void mla_splitkv(SplitKVParams p) {
   // ---- one 64-token tile: QK^T, softmax, PV ----
   // `next_q_unit` >= 0: this is the segment's last tile and the next segment's
   // queries are loaded once the QK product no longer needs the current ones.
-  // gather_slice(i) issues slice i of the next tile's gather (between QK
-  // k-steps) and warm_slice(k) slice k of the L2 warm-up (between PV steps).
+  // warm_slice(k) issues slice k of the L2 warm-up of the tile after next, and
+  // gather_slice(i) slice i of the next tile's gather (between QK k-steps).
   auto compute_tile = [&](const uint8_t* buf, int blk, uint64_t vmask,
                           int next_q_unit) __attribute__((always_inline)) {
     // S^T of this half's 32 tokens as two accumulation chains (even and odd
@@ -591,7 +608,6 @@ void mla_splitkv(SplitKVParams p) {
         const s16x8 pb = (kc >> 1) == half ? pk[kc & 1] : pp[kc & 1];
         const f32x16 c_in = (from_zero && kc == 0) ? f32x16{} : acc[ct];
         acc[ct] = mfma(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pb), c_in);
-        if (i < NWARM) warm_slice(i);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -729,17 +745,22 @@ hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, hipStre
   const int groups = p.num_parts * p.row_blocks;
   if (groups <= 0) return hipSuccess;
   const dim3 grid(groups), block(256);
-  if (d_qk == 576) {
-    if (sparse)
-      hipLaunchKernelGGL((mla_splitkv<576, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((mla_splitkv<576, false>), grid, block, 0, stream, p);
-  } else {
-    if (sparse)
-      hipLaunchKernelGGL((mla_splitkv<512, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((mla_splitkv<512, false>), grid, block, 0, stream, p);
-  }
+  // sparse rows are addressed with 32-bit byte offsets while the pool fits
+  const bool wide = uint64_t(p.num_rows) * uint64_t(d_qk) * 2 > 0xFFFFFFFFull;
+#define MLA_LAUNCH(D)                                                                        \
+  do {                                                                                       \
+    if (!sparse)                                                                             \
+      hipLaunchKernelGGL((mla_splitkv<D, false, false>), grid, block, 0, stream, p);         \
+    else if (!wide)                                                                          \
+      hipLaunchKernelGGL((mla_splitkv<D, true, false>), grid, block, 0, stream, p);          \
+    else                                                                                     \
+      hipLaunchKernelGGL((mla_splitkv<D, true, true>), grid, block, 0, stream, p);           \
+  } while (0)
+  if (d_qk == 576)
+    MLA_LAUNCH(576);
+  else
+    MLA_LAUNCH(512);
+#undef MLA_LAUNCH
   return hipGetLastError();
 }
 
