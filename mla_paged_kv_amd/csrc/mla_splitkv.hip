@@ -23,10 +23,10 @@
 //                      first 512 columns of the same tile.
 // Every K and V element read from LDS thus feeds 32 query rows.
 //
-// The gather of the next tile is issued in slices between the QK MFMAs, and
-// the L2 warm-up of the tile after next between the PV MFMAs, so their
-// address arithmetic runs in the shadow of the matrix cores.  The metadata of
-// the tile after next is read at the end of each step, and the next segment's
+// The gather of the next tile is issued in slices between the QK MFMAs, so
+// its address arithmetic runs in the shadow of the matrix cores.  The
+// metadata of the tile after next is read at the end of each step, and the
+// next segment's
 // queries are loaded as soon as the current segment's last QK product is
 // done.  A segment covering its whole unit writes bf16 O and fp32 LSE; a split
 // segment writes fp32 O and a base-2 LSE into its workspace slot for the
@@ -189,13 +189,10 @@ void mla_splitkv(SplitKVParams p) {
   constexpr int FMAX = CPR == 72 ? 8 : 16;  // swizzle values are below this
   constexpr int NKB = FMAX / 2;           // K-read bases (kk mod NKB)
   constexpr int NVB = FMAX / 4;           // V-read bases (ct mod NVB)
-  constexpr int kLines = kPage * D_QK * 2 / 128;     // 128-byte lines of a page
-  constexpr int NWARM = (kLines + 255) / 256;       // warm-up loads per wavefront
   static_assert(NLD % kWaves == 0 && (16 * CPR) % 64 == 0, "16 whole rows per wavefront");
-  static_assert(NLW <= 2 * KK && NWARM <= NSTEP, "gather slices fit the MFMA loops");
+  static_assert(2 * NLW <= KK + 1, "gather slices fit the QK loop");
   __shared__ __attribute__((aligned(1024))) uint8_t buf_a[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf_b[BUF];
-  __shared__ __attribute__((aligned(16))) uint32_t l2_sink[kWaves * 64];  // written, never read
   __shared__ __attribute__((aligned(16))) s16x8 x_p[kWaves][2][64];       // bf16 P of a pair half
   __shared__ float x_max[kWaves][32];                                      // row maxima of a half
   __shared__ float x_sum[kWaves][32];                                      // row sums of a half
@@ -362,33 +359,6 @@ void mla_splitkv(SplitKVParams p) {
     for (int i = 0; i < NLW; ++i) gather_one(g, dst, i, lane);
   };
 
-  // ---- L2 warm-up of the tile after next ----
-  // One dword of every 128-byte line of the tile is loaded into a scratch LDS
-  // slot that is never read: the lines are then in L2 when the tile's gather
-  // is issued one step later, so that gather waits for L2 instead of HBM and
-  // two tiles' worth of HBM reads are in flight per workgroup.  The warm-up is
-  // issued first in a step, so it has a whole step to complete before the
-  // next step's wait for the gather issued after it.
-  auto warm_one = [&](const TileMeta& m, int k) __attribute__((always_inline)) {
-    lds_void* dst = (lds_void*)(l2_sink + wave * 64);
-    if constexpr (SPARSE) {
-      constexpr int kRowLines = D_QK * 2 / 128;
-      const int line = min(wave + kWaves * k, kRowLines - 1);
-      const bool ok = m.idx >= 0 && m.idx < p.num_rows;
-      const int r = ok ? m.idx : 0;
-      if constexpr (WIDE) {
-        const uint8_t* row_ptr = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * RSB;
-        __builtin_amdgcn_global_load_lds(row_ptr + line * 128, dst, 4, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), dst, 4, r * RSB + line * 128, 0, 0, 0);
-      }
-    } else {
-      const int first = min(64 * (wave + kWaves * k), kLines - 64);  // uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(m.phys), dst, 4, (first + lane) * 128, 0, 0,
-                                              0);
-    }
-  };
-
   // ---- per-segment state ----
   // m_run: reference maximum (base 2, scaled) of the lane's row, identical in
   // both halves of a pair.  l_part: the row's sum of softmax numerators.
@@ -461,22 +431,20 @@ void mla_splitkv(SplitKVParams p) {
     }
   };
 
-  // The next tile's gather and the warm-up of the one after it, issued in
-  // slices from inside the tile computation; the step sets these up.
+  // The next tile's gather, issued in slices from inside the tile
+  // computation; the step sets it up.
   Gather nx_plan{0, 0, 0, 0};
   uint8_t* nx_dst = buf_b;
   int nx_ln = 0;
-  TileMeta nx_warm{0, 0, -1};
   auto gather_slice = [&](int i) __attribute__((always_inline)) {
     gather_one(nx_plan, nx_dst, i, nx_ln);
   };
-  auto warm_slice = [&](int k) __attribute__((always_inline)) { warm_one(nx_warm, k); };
 
   // ---- one 64-token tile: QK^T, softmax, PV ----
   // `next_q_unit` >= 0: this is the segment's last tile and the next segment's
   // queries are loaded once the QK product no longer needs the current ones.
-  // warm_slice(k) issues slice k of the L2 warm-up of the tile after next, and
-  // gather_slice(i) slice i of the next tile's gather (between QK k-steps).
+  // gather_slice(i) issues slice i of the next tile's gather (between QK
+  // k-steps).
   auto compute_tile = [&](const uint8_t* buf, int blk, uint64_t vmask,
                           int next_q_unit) __attribute__((always_inline)) {
     // S^T of this half's 32 tokens as two accumulation chains (even and odd
@@ -497,10 +465,8 @@ void mla_splitkv(SplitKVParams p) {
       if (kk + QD < KK) load_k(kk + QD);
       const int c = kk & 1;
       st[c] = mfma(kf[kk % (QD + 1)], qf[kk], kk < 2 ? f32x16{} : st[c]);
-      // the next tile's gather goes out early (two slices per k-step) so it
-      // has the rest of the tile to arrive
-      if (2 * kk < NLW) gather_slice(2 * kk);
-      if (2 * kk + 1 < NLW) gather_slice(2 * kk + 1);
+      // the next tile's gather, one slice every other k-step
+      if ((kk & 1) == 0 && kk / 2 < NLW) gather_slice(kk / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     st[0] += st[1];
@@ -655,9 +621,9 @@ void mla_splitkv(SplitKVParams p) {
     cmask = g0.vmask;
     if (!SPARSE || cmask != 0) gather_all(g0, buf_a);
   }
-  // tiles j+1 (gathered during the next step) and j+2 (warmed into L2 during
-  // the next step); the metadata of tile j+3 is read at the end of the step.
-  // All scalar metadata reads of a step happen after its compute: a scalar
+  // Tile j+1 is gathered during step j; metadata runs two tiles ahead of the
+  // gathers (that of tile j+3 is read at the end of step j).  All scalar
+  // metadata reads of a step happen after its compute: a scalar
   // load in flight shares the LDS wait counter and would turn every LDS
   // operand wait of the tile into a full drain.
   int ns, nblk, n2s, n2blk;
@@ -669,8 +635,6 @@ void mla_splitkv(SplitKVParams p) {
     nmeta = fetch_meta(ns, nblk);
     advance(ns, nblk, n2s, n2blk);
     if (n2s < seg_end) n2meta = fetch_meta(n2s, n2blk);
-#pragma unroll
-    for (int k = 0; k < NWARM; ++k) warm_one(nmeta, k);
   }
   // the current tile ends its segment / the unit whose queries follow it
   bool seg_last = cblk + 1 >= seg_b1(cs);
@@ -693,15 +657,12 @@ void mla_splitkv(SplitKVParams p) {
     nx_dst = nxt_buf;
     nx_ln = lane;
     asm volatile("" : "+v"(nx_ln));
-    nx_warm = n2meta;
     if (!SPARSE || cmask != 0) {
       compute_tile(cur_buf, cblk, cmask, next_q_unit);
     } else {
       if (next_q_unit >= 0) load_q(next_q_unit);
 #pragma unroll
       for (int i = 0; i < NLW; ++i) gather_slice(i);
-#pragma unroll
-      for (int k = 0; k < NWARM; ++k) warm_slice(k);
     }
     if (seg_last) {
       write_segment(qrow, seg_slot(cs), false);
