@@ -91,6 +91,7 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
   cp.off_num_splits = info->off_num_splits;
   cp.off_split_list = info->off_split_list;
   cp.num_split_units = info->num_split_units;
+  cp.max_splits = info->max_splits;
   cp.rows = info->rows;
   cp.s_q = s_q;
   cp.h_q = h_q;

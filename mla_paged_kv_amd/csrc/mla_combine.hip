@@ -2,9 +2,9 @@
 //
 // mla_combine merges the fp32 partial outputs of a split unit by their base-2
 // log-sum-exps, over active rows only (the DeepLink-org fork's active-head
-// combine).  Lane k of a wavefront holds the log-sum-exps of splits k, k+64,
-// ..., so up to 64 splits are merged in one pass (the fork's exact small-split
-// path, widened to wave64) and more in further passes.
+// combine).  Every split count is merged exactly in one kernel (the fork
+// special-cases small split counts; here the loop simply runs once for up to
+// 32 splits).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -30,72 +30,110 @@ __device__ __forceinline__ unsigned short f2bf(float x) {
 
 }  // namespace
 
-// One workgroup per (split unit, row).  Every wavefront derives the merged
-// log-sum-exp itself (lane k holds splits k, k+64, ...); the weighted sum of the
-// partial outputs is spread over the four wavefronts (wavefront w takes splits
-// w, w+4, ..., several loads in flight per lane) and reduced through LDS.
+// Two layouts, picked per launch from the largest split count:
+//  * ROW_WAVES = true (many splits): one workgroup per (split unit, row);
+//    wavefront w merges splits w, w+4, ... and the four results are merged
+//    through LDS;
+//  * ROW_WAVES = false (at most a few splits): one wavefront per (split unit,
+//    row), four rows per workgroup, no LDS.
+// A wavefront merges its splits against its own running maximum, issuing the
+// loads of up to kUnroll splits (their LSE and 8 partial-output columns per
+// lane) before using any, so the partial outputs are read in one round trip
+// per kUnroll splits with no separate pass over the LSEs.  Base-2
+// log-sum-exp throughout:
+//   lse = m + log2 sum_s 2^(lse_s - m),  O = sum_s 2^(lse_s - lse) O_s.
+template <bool ROW_WAVES>
 __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
-  constexpr int kWaves = 4, kUnroll = 4;
-  __shared__ f32x4 red[kWaves - 1][64][2];
+  constexpr int kWaves = 4, kUnroll = 8;
+  constexpr int kStride = ROW_WAVES ? kWaves : 1;  // split stride of a wavefront
+  __shared__ f32x4 red[ROW_WAVES ? kWaves : 1][64][2];  // per-wavefront weighted sums
+  __shared__ float red_m[kWaves], red_l[kWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int k = blockIdx.x / p.rows;
-  const int row = blockIdx.x - k * p.rows;
+  int k, row;
+  if constexpr (ROW_WAVES) {
+    k = blockIdx.x / p.rows;
+    row = blockIdx.x - k * p.rows;
+  } else {
+    const int groups = (p.rows + kWaves - 1) / kWaves;
+    k = blockIdx.x / groups;
+    row = (blockIdx.x - k * groups) * kWaves + wave;
+    if (row >= p.rows) return;
+  }
 
   const int32_t* meta = p.meta;
   const int u = meta[p.off_split_list + 2 * k];
   const int slot0 = meta[p.off_split_list + 2 * k + 1];
   const int nsplit = meta[p.off_num_splits + u + 1] - meta[p.off_num_splits + u];
   const float* lse_col = p.ws_lse + size_t(slot0) * p.rows + row;  // split s at s * rows
+  const float* o_col = p.ws_o + (size_t(slot0) * p.rows + row) * kDV + 8 * lane;
+  const size_t split_stride = size_t(p.rows) * kDV;
 
-  // merged LSE (base 2): max, then sum of 2^(lse - max)
-  float mx = -__builtin_inff();
-  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, lse_col[size_t(s) * p.rows]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  const float m_use = mx == -__builtin_inff() ? 0.f : mx;
-  float sum = 0.f;
-  for (int s = lane; s < nsplit; s += 64) sum += fast_exp2(lse_col[size_t(s) * p.rows] - m_use);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-  const bool empty = !(sum > 0.f);
-  const float lse2 = empty ? -__builtin_inff() : m_use + fast_log2(sum);
-
-  // weighted partial outputs; lane owns columns 8*lane .. 8*lane+7
+  // this wavefront's splits, merged online: m (running max), l, a0/a1
+  float m = -__builtin_inff(), l = 0.f;
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  if (!empty) {
-    const float* o_col = p.ws_o + (size_t(slot0) * p.rows + row) * kDV + 8 * lane;
-    const size_t split_stride = size_t(p.rows) * kDV;
-    for (int s0 = wave; s0 < nsplit; s0 += kWaves * kUnroll) {
-      f32x4 v0[kUnroll], v1[kUnroll];
-      float w[kUnroll];
+  for (int s0 = ROW_WAVES ? wave : 0; s0 < nsplit; s0 += kStride * kUnroll) {
+    f32x4 v0[kUnroll], v1[kUnroll];
+    float ls[kUnroll];
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int s = s0 + j * kWaves;
-        const bool ok = s < nsplit;
-        const float* src = o_col + size_t(ok ? s : s0) * split_stride;
-        v0[j] = *reinterpret_cast<const f32x4*>(src);
-        v1[j] = *reinterpret_cast<const f32x4*>(src + 4);
-        w[j] = ok ? fast_exp2(lse_col[size_t(ok ? s : s0) * p.rows] - lse2) : 0.f;
-      }
+    for (int j = 0; j < kUnroll; ++j) {
+      const int s = s0 + j * kStride;
+      const int sl = s < nsplit ? s : s0;  // in-bounds stand-in, weight 0 below
+      ls[j] = lse_col[size_t(sl) * p.rows];
+      const float* src = o_col + size_t(sl) * split_stride;
+      v0[j] = *reinterpret_cast<const f32x4*>(src);
+      v1[j] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    float mb = m;
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        a0 += w[j] * v0[j];
-        a1 += w[j] * v1[j];
+    for (int j = 0; j < kUnroll; ++j)
+      if (s0 + j * kStride < nsplit) mb = fmaxf(mb, ls[j]);
+    if (mb == -__builtin_inff()) continue;  // nothing but empty splits so far
+    const float alpha = fast_exp2(m - mb);  // 0 while m is -inf
+    l *= alpha;
+    a0 *= alpha;
+    a1 *= alpha;
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const float w = s0 + j * kStride < nsplit ? fast_exp2(ls[j] - mb) : 0.f;
+      l += w;
+      a0 += w * v0[j];
+      a1 += w * v1[j];
+    }
+    m = mb;
+  }
+  if constexpr (ROW_WAVES) {
+    red[wave][lane][0] = a0;
+    red[wave][lane][1] = a1;
+    if (lane == 0) {
+      red_m[wave] = m;
+      red_l[wave] = l;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mt = fmaxf(mt, red_m[w]);
+    float lt = 0.f;
+    a0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    a1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mt != -__builtin_inff()) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(red_m[w] - mt);  // 0 for a wavefront without splits
+        lt += sc * red_l[w];
+        a0 += sc * red[w][lane][0];
+        a1 += sc * red[w][lane][1];
       }
     }
+    m = mt;
+    l = lt;
   }
-  if (wave > 0) {
-    red[wave - 1][lane][0] = a0;
-    red[wave - 1][lane][1] = a1;
-  }
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    a0 += red[w][lane][0];
-    a1 += red[w][lane][1];
-  }
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  const float lse2 = empty ? -__builtin_inff() : m + fast_log2(l);
+  a0 *= inv;
+  a1 *= inv;
 
   int b, iq, h;
   if (p.sparse) {
@@ -119,8 +157,13 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   if (p.num_split_units <= 0 || p.rows <= 0) return hipSuccess;
-  const dim3 grid(p.num_split_units * p.rows), block(256);
-  hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);
+  const dim3 block(256);
+  if (p.max_splits > 16) {
+    hipLaunchKernelGGL(mla_combine<true>, dim3(p.num_split_units * p.rows), block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(mla_combine<false>, dim3(p.num_split_units * ((p.rows + 3) / 4)), block, 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 

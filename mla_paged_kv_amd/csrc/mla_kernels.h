@@ -38,6 +38,7 @@ struct CombineParams {
   uint16_t* out;
   float* lse;
   int32_t off_num_splits, off_split_list, num_split_units;
+  int32_t max_splits;  // most splits of any unit (picks the combine layout)
   int32_t rows, s_q, h_q, heads;
   int32_t sparse;
 };
