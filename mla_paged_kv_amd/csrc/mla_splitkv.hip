@@ -271,9 +271,8 @@ void mla_splitkv(SplitKVParams p) {
   };
 
   // ---- tile metadata, fetched ahead of the tile's gather ----
-  auto fetch_meta = [&](int s, int blk) __attribute__((always_inline)) -> TileMeta {
+  auto fetch_meta = [&](int u, int blk) __attribute__((always_inline)) -> TileMeta {
     TileMeta m{0, 0, -1};
-    const int u = seg_u(s);
     if constexpr (SPARSE) {
       const int pos = blk * kPage + lane;
       m.idx = pos < p.topk ? p.indices[size_t(u) * p.topk + pos] : -1;
@@ -588,57 +587,67 @@ void mla_splitkv(SplitKVParams p) {
   };
 
   // ---- tile stream of the part ----
-  // next tile after (s, blk), skipping segments without tiles
-  auto advance = [&](int s, int blk, int& s2, int& blk2) __attribute__((always_inline)) {
-    if (blk + 1 < seg_b1(s)) {
-      s2 = s;
-      blk2 = blk + 1;
-      return;
-    }
-    s2 = s + 1;
+  // A tile of the stream: its segment, block, unit, and whether it is the
+  // segment's last.  The segment of the furthest tile looked up is cached
+  // (la_*), so stepping within a segment reads no metadata, and a step issues
+  // one independent scalar load (the block-table entry) that nothing waits
+  // for until two steps later.
+  struct Tile {
+    int s, blk, u;
+    bool last;
+  };
+  int la_s = seg_begin, la_u = 0, la_b1 = 0;  // cached segment
+  auto load_seg = [&](int s2) __attribute__((always_inline)) {
+    la_s = s2;
+    la_u = seg_u(s2);
+    la_b1 = seg_b1(s2);
+  };
+  auto first_tile_from = [&](int s2) __attribute__((always_inline)) -> Tile {
+    // first tile at or after segment s2, skipping segments without tiles
     while (s2 < seg_end && seg_b0(s2) == seg_b1(s2)) ++s2;
-    blk2 = s2 < seg_end ? seg_b0(s2) : 0;
+    if (s2 >= seg_end) return Tile{seg_end, 0, 0, true};
+    load_seg(s2);
+    const int b0 = seg_b0(s2);
+    return Tile{s2, b0, la_u, b0 + 1 >= la_b1};
+  };
+  // the tile after t (t is in the cached segment)
+  auto next_tile = [&](const Tile& t) __attribute__((always_inline)) -> Tile {
+    if (t.s >= seg_end) return t;
+    if (!t.last) return Tile{t.s, t.blk + 1, t.u, t.blk + 2 >= la_b1};
+    return first_tile_from(t.s + 1);
   };
 
   // leading segments without tiles
-  int cs = seg_begin;
-  while (cs < seg_end && seg_b0(cs) == seg_b1(cs)) {
-    write_segment(row_index(seg_u(cs), row), seg_slot(cs), true);
-    ++cs;
+  int cs0 = seg_begin;
+  while (cs0 < seg_end && seg_b0(cs0) == seg_b1(cs0)) {
+    write_segment(row_index(seg_u(cs0), row), seg_slot(cs0), true);
+    ++cs0;
   }
-  if (cs >= seg_end) return;
+  if (cs0 >= seg_end) return;
 
   // first tile: gathered into buf_a before the stream starts
-  int cblk = seg_b0(cs);
+  Tile ct = first_tile_from(cs0);
   uint64_t cmask;
   {
-    const TileMeta m0 = fetch_meta(cs, cblk);
+    const TileMeta m0 = fetch_meta(ct.u, ct.blk);
     if (!SPARSE) n_vis = visible(m0.len);
-    qrow = row_index(seg_u(cs), row);
-    load_q(seg_u(cs));
+    qrow = row_index(ct.u, row);
+    load_q(ct.u);
     reset_state();
-    const Gather g0 = plan_gather(cblk, m0);
+    const Gather g0 = plan_gather(ct.blk, m0);
     cmask = g0.vmask;
     if (!SPARSE || cmask != 0) gather_all(g0, buf_a);
   }
   // Tile j+1 is gathered during step j; metadata runs two tiles ahead of the
   // gathers (that of tile j+3 is read at the end of step j).  All scalar
-  // metadata reads of a step happen after its compute: a scalar
-  // load in flight shares the LDS wait counter and would turn every LDS
-  // operand wait of the tile into a full drain.
-  int ns, nblk, n2s, n2blk;
-  advance(cs, cblk, ns, nblk);
+  // metadata reads of a step happen after its compute: a scalar load in
+  // flight shares the LDS wait counter and would turn every LDS operand wait
+  // of the tile into a full drain.
+  Tile nt = next_tile(ct);
+  Tile n2t = next_tile(nt);
   TileMeta nmeta{0, 0, -1}, n2meta{0, 0, -1};
-  n2s = seg_end;
-  n2blk = 0;
-  if (ns < seg_end) {
-    nmeta = fetch_meta(ns, nblk);
-    advance(ns, nblk, n2s, n2blk);
-    if (n2s < seg_end) n2meta = fetch_meta(n2s, n2blk);
-  }
-  // the current tile ends its segment / the unit whose queries follow it
-  bool seg_last = cblk + 1 >= seg_b1(cs);
-  int next_q_unit = (seg_last && ns < seg_end) ? seg_u(ns) : -1;
+  if (nt.s < seg_end) nmeta = fetch_meta(nt.u, nt.blk);
+  if (n2t.s < seg_end) n2meta = fetch_meta(n2t.u, n2t.blk);
 
   // One step computes the tile in `cur_buf` while the next one streams into
   // `nxt_buf`.  The two buffers are distinct LDS objects named statically at
@@ -646,52 +655,46 @@ void mla_splitkv(SplitKVParams p) {
   // asynchronous writes into the other and does not wait for those writes.
   auto step = [&](const uint8_t* cur_buf, uint8_t* nxt_buf) __attribute__((always_inline)) -> bool {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);  // loop-carried in AGPRs
+    for (int ct_ = 0; ct_ < NCT; ++ct_) pin_agpr(acc[ct_]);  // loop-carried in AGPRs
     wait_vmem();
     __syncthreads();
-    const bool has_next = ns < seg_end, has_next2 = n2s < seg_end;
+    const bool has_next = nt.s < seg_end;
     // Without a next tile (or a valid index in it) the slices load page 0 /
     // cache row 0 instead: harmless, in bounds and branch-free.
-    nx_plan = plan_gather(nblk, nmeta);
+    nx_plan = plan_gather(nt.blk, nmeta);
     const uint64_t nmask = has_next ? nx_plan.vmask : 0;
     nx_dst = nxt_buf;
     nx_ln = lane;
     asm volatile("" : "+v"(nx_ln));
+    const int next_q_unit = (ct.last && has_next) ? nt.u : -1;
     if (!SPARSE || cmask != 0) {
-      compute_tile(cur_buf, cblk, cmask, next_q_unit);
+      compute_tile(cur_buf, ct.blk, cmask, next_q_unit);
     } else {
       if (next_q_unit >= 0) load_q(next_q_unit);
 #pragma unroll
       for (int i = 0; i < NLW; ++i) gather_slice(i);
     }
-    if (seg_last) {
-      write_segment(qrow, seg_slot(cs), false);
-      for (int e = cs + 1; e < ns; ++e)  // segments without tiles passed over
+    if (ct.last) {
+      write_segment(qrow, seg_slot(ct.s), false);
+      const int e_end = has_next ? nt.s : seg_end;
+      for (int e = ct.s + 1; e < e_end; ++e)  // segments without tiles passed over
         write_segment(row_index(seg_u(e), row), seg_slot(e), true);
       if (has_next) {
-        qrow = row_index(seg_u(ns), row);
+        qrow = row_index(nt.u, row);
         if (!SPARSE) n_vis = visible(nmeta.len);
         reset_state();
       }
     }
     if (!has_next) return false;
-    int n3s = seg_end, n3blk = 0;
+    const Tile n3t = next_tile(n2t);
     TileMeta n3meta{0, 0, -1};
-    if (has_next2) {
-      advance(n2s, n2blk, n3s, n3blk);
-      if (n3s < seg_end) n3meta = fetch_meta(n3s, n3blk);
-    }
-    cs = ns;
-    cblk = nblk;
+    if (n3t.s < seg_end) n3meta = fetch_meta(n3t.u, n3t.blk);
+    ct = nt;
     cmask = nmask;
-    ns = n2s;
-    nblk = n2blk;
+    nt = n2t;
     nmeta = n2meta;
-    n2s = n3s;
-    n2blk = n3blk;
+    n2t = n3t;
     n2meta = n3meta;
-    seg_last = cblk + 1 >= seg_b1(cs);
-    next_q_unit = (seg_last && ns < seg_end) ? seg_u(ns) : -1;
     return true;
   };
   for (;;) {
