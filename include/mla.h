@@ -134,6 +134,44 @@ int mla_get_metadata(const int32_t* cache_seqlens_host, int32_t batch, int32_t s
                      int32_t num_cus, int32_t num_parts, int32_t* meta_host,
                      size_t meta_capacity_ints, mla_sched_info* info);
 
+/*
+ * mla_get_metadata_device -- the same tile scheduler run on the GPU, for
+ * sequence lengths that are already in device memory (the pages call
+ * get_mla_metadata on the device tensor of cache lengths once per decode step:
+ * deepep.org usage example).  It enqueues one single-workgroup kernel on
+ * `stream` and returns without synchronising, so a decode step needs no host
+ * round trip and can be captured in a HIP graph.  The device array it writes
+ * is bit-identical to mla_get_metadata's output for the same lengths.
+ *
+ *   cache_seqlens_dev  [batch] int32, device.  Dense mode only (topk == 0);
+ *                      may be NULL in sparse mode.  Read when the kernel runs.
+ *   batch ... num_parts  as for mla_get_metadata.
+ *   meta_dev           [meta_capacity_ints] int32, device: receives the
+ *                      metadata array.  meta_capacity_ints must be at least
+ *                      mla_metadata_capacity(units, parts).
+ *   info               host: receives a header of upper bounds, which is what
+ *                      the decode calls and mla_workspace_bytes need: num_parts
+ *                      = the target part count P, num_segments = U + P - 1,
+ *                      total_slots = min(U + P - 1, 2(P - 1)), num_split_units
+ *                      = min(U, P - 1), max_splits = P; quota and total_cost
+ *                      are -1; off_segs, off_num_splits and off_split_list are
+ *                      -1, which tells the kernels to read the exact counts
+ *                      and offsets from the device header; total_ints = the
+ *                      capacity.  Pass this info with meta_dev to the decode
+ *                      calls, which then size their grids by the bounds.
+ *   stream             hipStream_t (NULL = the null stream).
+ *
+ * Limits: at most 4096 units and 1024 parts (MLA_E_NOTSUP beyond).  A length
+ * below 0 or above 2^24 cannot be reported to the host without a round trip:
+ * the kernel then writes an empty schedule (num_parts = num_split_units = 0,
+ * total_ints = -1 in the device header) and a decode call with it writes
+ * nothing.  Other errors as for mla_get_metadata, plus MLA_E_HIP.
+ */
+int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int32_t batch, int32_t s_q,
+                            int32_t h_q, int32_t h_kv, int32_t topk, int32_t active_h_q,
+                            int32_t num_cus, int32_t num_parts, int32_t* meta_dev,
+                            size_t meta_capacity_ints, mla_sched_info* info, void* stream);
+
 /* Workspace bytes a decode call with this metadata needs (0 if nothing is
  * split): fp32 partial outputs [total_slots, rows, d_v] then, 256-byte
  * aligned, fp32 partial log-sum-exps [total_slots, rows]. */

@@ -10,6 +10,7 @@ HIP kernels; there is no fallback.  ``libmla.so`` is built in-tree by
 Entry points mirror the C ABI names:
 
 * ``mla_get_metadata``   -- tile scheduler (host), once per decode step
+* ``mla_get_metadata_device`` -- the same scheduler as a GPU kernel (no sync)
 * ``mla_decode_paged``   -- dense paged decode, once per layer
 * ``mla_decode_sparse``  -- top-k sparse decode, once per layer
 
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     mla_decode_paged,
     mla_decode_sparse,
     mla_get_metadata,
+    mla_get_metadata_device,
     mla_workspace_bytes,
 )
 
@@ -39,5 +41,6 @@ __all__ = [
     "mla_decode_paged",
     "mla_decode_sparse",
     "mla_get_metadata",
+    "mla_get_metadata_device",
     "mla_workspace_bytes",
 ]

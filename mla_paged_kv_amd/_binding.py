@@ -62,6 +62,9 @@ def _load():
     lib.mla_metadata_capacity.argtypes = [i32, i32]
     lib.mla_get_metadata.restype = ctypes.c_int
     lib.mla_get_metadata.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, pinfo]
+    lib.mla_get_metadata_device.restype = ctypes.c_int
+    lib.mla_get_metadata_device.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+                                            pinfo, vp]
     lib.mla_workspace_bytes.restype = sz
     lib.mla_workspace_bytes.argtypes = [pinfo, i32]
     lib.mla_decode_paged.restype = ctypes.c_int
@@ -88,14 +91,19 @@ def _check(rc: int, what: str) -> int:
 
 
 class Metadata:
-    """Tile-scheduler output: host header + arrays, and the device copy."""
+    """Tile-scheduler output: host header + arrays, and the device copy.
 
-    def __init__(self, info: MlaSchedInfo, meta_host: np.ndarray, meta_dev, *, sparse: bool,
-                 batch: int, s_q: int, h_q: int, topk: int):
+    For metadata built on the device (:func:`mla_get_metadata_device`),
+    ``meta_host`` is None and ``info`` holds upper bounds; :meth:`exact`
+    copies the device array to the host (synchronising)."""
+
+    def __init__(self, info: MlaSchedInfo, meta_host, meta_dev, *, sparse: bool,
+                 batch: int, s_q: int, h_q: int, topk: int, device_built: bool = False):
         self.info = info
         self.meta_host = meta_host
         self.meta_dev = meta_dev
         self.sparse = sparse
+        self.device_built = device_built
         self.batch, self.s_q, self.h_q, self.topk = batch, s_q, h_q, topk
 
     def __getattr__(self, name):
@@ -107,16 +115,25 @@ class Metadata:
     def heads(self) -> int:
         return self.info.rows if self.sparse else self.info.rows // self.s_q
 
+    def exact(self) -> np.ndarray:
+        """The metadata array as the decode kernels see it (header + arrays)."""
+        if not self.device_built:
+            return self.meta_host
+        m = self.meta_dev.cpu().numpy()
+        return m[:max(16, int(m[15]))]
+
     @property
     def num_splits(self) -> np.ndarray:
         """Cumulative segment count per unit, [num_units + 1]."""
-        o = self.info.off_num_splits
-        return self.meta_host[o:o + self.info.num_units + 1]
+        m = self.exact()
+        o = int(m[13])
+        return m[o:o + self.info.num_units + 1]
 
     @property
     def segments(self) -> np.ndarray:
-        o = self.info.off_segs
-        return self.meta_host[o:o + 4 * self.info.num_segments].reshape(-1, 4)
+        m = self.exact()
+        o = int(m[12])
+        return m[o:o + 4 * int(m[1])].reshape(-1, 4)
 
     def workspace_bytes(self, dv: int = 512) -> int:
         return int(_load().mla_workspace_bytes(ctypes.byref(self.info), dv))
@@ -165,6 +182,49 @@ def mla_get_metadata(cache_seqlens, s_q: int, h_q: int, h_kv: int = 1, topk: int
     meta = meta[:info.total_ints].copy()
     meta_dev = torch.from_numpy(meta).to(device) if upload else None
     return Metadata(info, meta, meta_dev, sparse=topk > 0, batch=batch, s_q=s_q, h_q=h_q, topk=topk)
+
+
+def mla_get_metadata_device(cache_seqlens, s_q: int, h_q: int, h_kv: int = 1, topk: int = 0,
+                            active_h_q: int = 0, num_parts: int = 0, num_cus: int | None = None,
+                            batch: int | None = None, device=None, meta_out=None) -> Metadata:
+    """Tile scheduler on the GPU, enqueued on the current stream (no
+    synchronisation; capturable in a CUDA/HIP graph).  ``cache_seqlens``: [batch]
+    int32 device tensor (may be None in sparse mode, then give ``batch``).
+    ``meta_out``: optional preallocated int32 device tensor of at least
+    ``mla_metadata_capacity`` ints (reused across graph replays)."""
+    lib = _load()
+    if cache_seqlens is not None:
+        _need(isinstance(cache_seqlens, torch.Tensor) and cache_seqlens.is_cuda
+              and cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous()
+              and cache_seqlens.dim() == 1, "cache_seqlens must be a contiguous int32 [B] GPU tensor")
+        batch = int(cache_seqlens.shape[0])
+        device = cache_seqlens.device
+    _need(batch is not None, "give cache_seqlens or batch")
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    if num_cus is None:
+        num_cus = _num_cus(device) if num_parts == 0 else 0
+    units = batch * s_q if topk > 0 else batch
+    if num_parts > 0:
+        target = num_parts
+    else:
+        per_unit = s_q if topk == 0 else 1
+        target = max(int(lib.mla_default_num_parts(per_unit * h, max(1, num_cus)))
+                     for h in {max(1, active_h_q or h_q), h_q})
+    cap = int(lib.mla_metadata_capacity(units, max(1, target)))
+    if meta_out is None:
+        meta_out = torch.empty(cap, dtype=torch.int32, device=device)
+    _need(meta_out.dtype == torch.int32 and meta_out.is_cuda and meta_out.is_contiguous(),
+          "meta_out must be a contiguous int32 GPU tensor")
+    info = MlaSchedInfo()
+    rc = lib.mla_get_metadata_device(_ptr(cache_seqlens), batch, s_q, h_q, h_kv, topk, active_h_q,
+                                     int(num_cus), num_parts, _ptr(meta_out), meta_out.numel(),
+                                     ctypes.byref(info), _stream(device))
+    _check(rc, "mla_get_metadata_device")
+    if rc == MLA_W_ACTIVE_FALLBACK:
+        warnings.warn(f"active_h_q={active_h_q} invalid for h_q={h_q}: all heads are computed")
+    return Metadata(info, None, meta_out, sparse=topk > 0, batch=batch, s_q=s_q, h_q=h_q,
+                    topk=topk, device_built=True)
 
 
 def mla_workspace_bytes(meta: Metadata, dv: int = 512) -> int:
@@ -224,9 +284,10 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
     _need(d_kv == d_qk, "kvcache row width must equal q's d_qk")
     _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
     _need(cache_seqlens.shape == (B,), "cache_seqlens must be [B]")
-    segs = meta.segments
-    _need(len(segs) == 0 or int(segs[:, 2].max()) <= block_table.shape[1],
-          "cache_seqlens of the metadata need more blocks than block_table has columns")
+    if not meta.device_built:  # (device metadata is not read back: no synchronisation)
+        segs = meta.segments
+        _need(len(segs) == 0 or int(segs[:, 2].max()) <= block_table.shape[1],
+              "cache_seqlens of the metadata need more blocks than block_table has columns")
     if softmax_scale is None:
         softmax_scale = d_qk ** -0.5
     out, lse, workspace, ws_bytes = _prep_outputs(q, meta, dv, workspace, out, lse)

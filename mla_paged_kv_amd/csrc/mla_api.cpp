@@ -92,6 +92,12 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
   cp.off_split_list = info->off_split_list;
   cp.num_split_units = info->num_split_units;
   cp.max_splits = info->max_splits;
+  if (info->off_split_list < 0) {
+    // device-built metadata: the host knows bounds only; pick the combine
+    // layout from the mean number of parts per unit
+    const int32_t units = info->num_units > 0 ? info->num_units : 1;
+    cp.max_splits = (info->num_parts + units - 1) / units + 1;
+  }
   cp.rows = info->rows;
   cp.s_q = s_q;
   cp.h_q = h_q;

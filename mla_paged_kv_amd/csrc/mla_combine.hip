@@ -62,9 +62,18 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
   }
 
   const int32_t* meta = p.meta;
-  const int u = meta[p.off_split_list + 2 * k];
-  const int slot0 = meta[p.off_split_list + 2 * k + 1];
-  const int nsplit = meta[p.off_num_splits + u + 1] - meta[p.off_num_splits + u];
+  // offsets and the split-unit count come from the host when it built the
+  // metadata, else (negative offsets) from the device header, and the grid
+  // then covers an upper bound of the split units
+  int off_sl = p.off_split_list, off_ns = p.off_num_splits;
+  if (off_sl < 0) {
+    if (k >= meta[3]) return;
+    off_ns = meta[13];
+    off_sl = meta[14];
+  }
+  const int u = meta[off_sl + 2 * k];
+  const int slot0 = meta[off_sl + 2 * k + 1];
+  const int nsplit = meta[off_ns + u + 1] - meta[off_ns + u];
   const float* lse_col = p.ws_lse + size_t(slot0) * p.rows + row;  // split s at s * rows
   const float* o_col = p.ws_o + (size_t(slot0) * p.rows + row) * kDV + 8 * lane;
   const size_t split_stride = size_t(p.rows) * kDV;

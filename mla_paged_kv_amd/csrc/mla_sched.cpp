@@ -166,6 +166,35 @@ int build_schedule(const int64_t* len, int32_t n, int32_t parts, int32_t rows,
   return MLA_OK;
 }
 
+int resolve_sched_shape(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t topk,
+                        int32_t active_h_q, int32_t num_cus, int32_t num_parts, SchedShape* out) {
+  if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || topk < 0 || active_h_q < 0 ||
+      num_cus < 0 || num_parts < 0)
+    return set_error(MLA_E_INVAL, "get_metadata: negative or zero shape");
+  if (h_q % h_kv != 0) return set_error(MLA_E_INVAL, "get_metadata: h_q %% h_kv != 0");
+  if (num_parts == 0 && num_cus == 0)
+    return set_error(MLA_E_INVAL, "get_metadata: give num_cus or num_parts");
+  int rc = MLA_OK;
+  int32_t heads = h_q;
+  if (active_h_q != 0 && active_h_q != h_q) {
+    if (active_h_q <= h_q && active_h_q % 8 == 0) {
+      heads = active_h_q;
+    } else {
+      rc = MLA_W_ACTIVE_FALLBACK;  // fail closed: compute every head
+    }
+  }
+  const int32_t per_kv_head = heads / h_kv > 0 ? heads / h_kv : 1;
+  const bool sparse = topk > 0;
+  const int64_t units64 = sparse ? int64_t(batch) * s_q : int64_t(batch);
+  if (units64 > (1 << 24)) return set_error(MLA_E_INVAL, "get_metadata: too many units");
+  const int64_t rows64 = sparse ? per_kv_head : int64_t(s_q) * per_kv_head;
+  if (rows64 > (1 << 24)) return set_error(MLA_E_INVAL, "get_metadata: too many rows per unit");
+  out->units = int32_t(units64);
+  out->rows = int32_t(rows64);
+  out->parts = num_parts > 0 ? num_parts : default_num_parts(out->rows, num_cus);
+  return rc;
+}
+
 }  // namespace mla
 
 extern "C" {
@@ -184,33 +213,16 @@ int mla_get_metadata(const int32_t* cache_seqlens_host, int32_t batch, int32_t s
                      size_t meta_capacity_ints, mla_sched_info* info) {
   using namespace mla;
   clear_error();
-  if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || topk < 0 || active_h_q < 0 ||
-      num_cus < 0 || num_parts < 0)
-    return set_error(MLA_E_INVAL, "get_metadata: negative or zero shape");
-  if (h_q % h_kv != 0) return set_error(MLA_E_INVAL, "get_metadata: h_q %% h_kv != 0");
   if (meta_host == nullptr || info == nullptr)
     return set_error(MLA_E_INVAL, "get_metadata: null meta_host/info");
   if (topk == 0 && batch > 0 && cache_seqlens_host == nullptr)
     return set_error(MLA_E_INVAL, "get_metadata: dense mode needs cache_seqlens_host");
-  if (num_parts == 0 && num_cus == 0)
-    return set_error(MLA_E_INVAL, "get_metadata: give num_cus or num_parts");
-
-  int rc = MLA_OK;
-  int32_t heads = h_q;
-  if (active_h_q != 0 && active_h_q != h_q) {
-    if (active_h_q <= h_q && active_h_q % 8 == 0) {
-      heads = active_h_q;
-    } else {
-      rc = MLA_W_ACTIVE_FALLBACK;  // fail closed: compute every head
-    }
-  }
-  const int32_t per_kv_head = heads / h_kv > 0 ? heads / h_kv : 1;
+  SchedShape sh;
+  const int rc = resolve_sched_shape(batch, s_q, h_q, h_kv, topk, active_h_q, num_cus, num_parts,
+                                     &sh);
+  if (rc < 0) return rc;
+  const int32_t units = sh.units;
   const bool sparse = topk > 0;
-  const int64_t units64 = sparse ? int64_t(batch) * s_q : int64_t(batch);
-  if (units64 > (1 << 24)) return set_error(MLA_E_INVAL, "get_metadata: too many units");
-  const int32_t units = int32_t(units64);
-  const int32_t rows = sparse ? per_kv_head : s_q * per_kv_head;
-  const int32_t parts = num_parts > 0 ? num_parts : default_num_parts(rows, num_cus);
 
   // unit lengths, on the stack for small batches
   constexpr int32_t kStack = 4096;
@@ -232,7 +244,7 @@ int mla_get_metadata(const int32_t* cache_seqlens_host, int32_t batch, int32_t s
   if (bad >= 0) {
     st = set_error(MLA_E_INVAL, "get_metadata: cache_seqlens[%d] < 0", bad);
   } else {
-    st = build_schedule(len, units, parts, rows, meta_host, meta_capacity_ints, info);
+    st = build_schedule(len, units, sh.parts, sh.rows, meta_host, meta_capacity_ints, info);
   }
   delete[] heap_len;
   if (st != MLA_OK) return st;

@@ -211,6 +211,9 @@ void mla_splitkv(SplitKVParams p) {
   if (part >= p.num_parts) return;
 
   cint* meta = as_const(p.meta);
+  // the grid covers p.num_parts parts, the device header says how many exist
+  // (fewer only when the metadata was built on the device)
+  if (part >= meta[0]) return;
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
   cint* segs = meta + meta[12];

@@ -15,7 +15,7 @@ from hypothesis import given, settings, strategies as st
 
 import mla_paged_kv_amd as mla
 from mla_paged_kv_amd import _binding as B
-from oracle.schedule import ref_num_parts, ref_schedule
+from oracle.schedule import ref_num_parts, ref_schedule, unpack_schedule as unpack
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla.h")
@@ -37,7 +37,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     names = header_functions()
-    for n in ["mla_get_metadata", "mla_decode_paged", "mla_decode_sparse", "mla_workspace_bytes",
+    for n in ["mla_get_metadata", "mla_get_metadata_device", "mla_decode_paged", "mla_decode_sparse", "mla_workspace_bytes",
               "mla_strerror", "mla_last_error", "mla_version", "mla_default_num_parts",
               "mla_metadata_capacity"]:
         assert n in names
@@ -144,6 +144,47 @@ def test_get_metadata_errors(lib):
 
 
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def test_get_metadata_device_rejects_before_launch(lib):
+    """Every rejected call returns before the scheduler kernel is enqueued."""
+    info = B.MlaSchedInfo()
+
+    def call(sl=FAKE, batch=2, s_q=1, h_q=16, h_kv=1, topk=0, act=0, cus=0, P=4, meta=FAKE,
+             cap=10 ** 6):
+        return lib.mla_get_metadata_device(sl, batch, s_q, h_q, h_kv, topk, act, cus, P, meta, cap,
+                                           ctypes.byref(info), None)
+
+    assert call(meta=None) == -1                       # no output array
+    assert call(sl=None) == -1                         # dense mode without lengths
+    assert call(h_q=15, h_kv=2) == -1                  # h_q % h_kv
+    assert call(P=0, cus=0) == -1                      # neither parts nor CUs
+    assert call(s_q=0) == -1
+    assert call(batch=4097) == -2                      # more units than one workgroup holds
+    assert b"4096" in lib.mla_last_error()
+    assert call(batch=1025, s_q=4, topk=64, sl=None) == -2   # sparse units = batch * s_q
+    assert call(P=1025) == -2
+    assert call(cap=int(lib.mla_metadata_capacity(2, 4)) - 1) == -3
+    assert call(topk=(1 << 24) + 1, sl=None) == -1
+
+
+def test_device_metadata_host_header_is_a_bound(lib):
+    """The host header of device-built metadata bounds every count the
+    reference scheduler produces for any lengths (checked on random lengths)."""
+    rng = np.random.default_rng(5)
+    for U, P in ((1, 1), (7, 3), (64, 256), (300, 16), (16, 1024)):
+        for _ in range(20):
+            lens = rng.integers(0, 20000, U)
+            lens[rng.random(U) < 0.3] = rng.integers(0, 100)
+            r = unpack(ref_schedule(lens.tolist(), P, 64))
+            bound_segments = U + P - 1
+            bound_slots = min(U + P - 1, 2 * (P - 1))
+            assert r["num_parts"] <= P
+            assert r["num_segments"] <= bound_segments
+            assert r["total_slots"] <= bound_slots
+            assert r["num_split_units"] <= min(U, P - 1)
+            assert r["max_splits"] <= P
+            assert r["total_ints"] <= lib.mla_metadata_capacity(U, P)
 
 
 def _paged(lib, info, **kw):
