@@ -16,6 +16,9 @@ splits):
   "Usage / MLA Decoding").
 * ``ref_decode_sparse``  -- token-level sparse decode through an ``indices``
   tensor (same README, "Sparse Attention (indices tensor)").
+* ``fp8.dequant_rows``   -- the "FP8 with scale" cache row (upstream README,
+  "FP8 KV Cache"): both decode functions accept such a cache and dequantize
+  the rows they read.
 * ``ref_schedule``       -- the reference tile scheduler.  The pages give only
   its purpose (metadata from sequence lengths and the head configuration that
   spreads variable-length work over compute units); the algorithm is this
@@ -25,11 +28,13 @@ splits):
   characterise the greedy partition (coverage, budget, maximality, slot
   numbering), checked in ``tests/test_oracle_schedule.py``.
 """
+from . import fp8
 from .decode import ref_decode_paged, ref_decode_sparse, ref_attend_rows
 from .schedule import (ref_schedule, ref_num_parts, unpack_schedule,
                        SPLIT_OVERHEAD_BLOCKS, PAGE_BLOCK)
 
 __all__ = [
+    "fp8",
     "ref_decode_paged",
     "ref_decode_sparse",
     "ref_attend_rows",

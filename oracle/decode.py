@@ -41,6 +41,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import fp8
+
 
 def _to_f64(x) -> np.ndarray:
     """Exact float64 copy of a numpy array or torch tensor (bf16 included)."""
@@ -91,17 +93,31 @@ def visible_len(L: int, s_q: int, i: int, causal: bool) -> int:
     return max(0, min(L, L - s_q + i + 1))
 
 
+def _is_fp8(kv) -> bool:
+    """An "FP8 with scale" cache: bytes, 656 per row (see ``oracle.fp8``)."""
+    return str(kv.dtype) in ("uint8", "torch.uint8") and kv.shape[-1] == fp8.ROW_BYTES
+
+
 def _gather_f64(kv, rows_index):
-    """kv[rows_index] as float64, converting only the gathered rows."""
+    """kv[rows_index] as float64, converting (or dequantizing) only the gathered rows."""
     try:
         import torch
 
         if isinstance(kv, torch.Tensor):
             ix = tuple(torch.as_tensor(np.asarray(a), dtype=torch.long) for a in rows_index)
+            if _is_fp8(kv):
+                return fp8.dequant_rows(kv[ix].numpy())
             return kv[ix].to(dtype=torch.float64).numpy()
     except ImportError:  # pragma: no cover
         pass
+    if _is_fp8(kv):
+        return fp8.dequant_rows(np.asarray(kv[rows_index]))
     return np.asarray(kv[rows_index], dtype=np.float64)
+
+
+def _row_width(kv) -> int:
+    """Values per cache row: d_qk (576 for an FP8 cache)."""
+    return fp8.NOPE + fp8.ROPE if _is_fp8(kv) else kv.shape[-1]
 
 
 def ref_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, causal: bool,
@@ -109,7 +125,9 @@ def ref_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, causal: bo
     """Dense paged MLA decode, FP64.
 
     q            [B, s_q, h_q, d_qk]
-    kvcache      [num_blocks, page, h_kv, d_qk]   (page = 64 in every config)
+    kvcache      [num_blocks, page, h_kv, d_qk]   (page = 64 in every config), or
+                 [num_blocks, page, h_kv, 656] uint8 in the FP8-with-scale format
+                 (d_qk = 576; rows dequantized by ``oracle.fp8.dequant_rows``)
     block_table  [B, max_blocks] int; entry j of row b is the physical block of
                  logical positions [j*page, (j+1)*page) of request b
     cache_seqlens[B] int; tokens in the cache of request b (the s_q new tokens
@@ -125,8 +143,8 @@ def ref_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, causal: bo
     bt = _to_i64(block_table)
     sl = _to_i64(cache_seqlens)
     B, s_q, h_q, d_qk = qf.shape
-    _, page, h_kv, d_kv = kvcache.shape
-    assert d_kv == d_qk and h_q % h_kv == 0 and dv <= d_qk
+    _, page, h_kv, _ = kvcache.shape
+    assert _row_width(kvcache) == d_qk and h_q % h_kv == 0 and dv <= d_qk
     group = h_q // h_kv
     head_list = list(range(h_q)) if heads is None else list(heads)
     O = np.full((B, s_q, h_q, dv), np.nan)
@@ -153,7 +171,8 @@ def ref_decode_sparse(q, kvcache, indices, dv: int, softmax_scale: float, heads=
     """Top-k sparse MLA decode, FP64.
 
     q        [B, s_q, h_q, d_qk]
-    kvcache  [num_blocks, page, h_kv, d_qk]; row e = block e // page, offset e % page
+    kvcache  [num_blocks, page, h_kv, d_qk] (or 656-byte FP8 rows, as for dense);
+             row e = block e // page, offset e % page
     indices  [B, s_q, topk] int; entry = block*page + offset, invalid if < 0 or
              >= num_blocks*page (those are dropped)
     heads    optional iterable of heads to compute (default: all); sparse decode
@@ -165,8 +184,8 @@ def ref_decode_sparse(q, kvcache, indices, dv: int, softmax_scale: float, heads=
     qf = _to_f64(q)
     idx = _to_i64(indices)
     B, s_q, h_q, d_qk = qf.shape
-    nblk, page, h_kv, d_kv = kvcache.shape
-    assert d_kv == d_qk and h_q % h_kv == 0 and dv <= d_qk
+    nblk, page, h_kv, _ = kvcache.shape
+    assert _row_width(kvcache) == d_qk and h_q % h_kv == 0 and dv <= d_qk
     group = h_q // h_kv
     head_list = list(range(h_q)) if heads is None else list(heads)
     O = np.full((B, s_q, h_q, dv), np.nan)
