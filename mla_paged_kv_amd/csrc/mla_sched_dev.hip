@@ -13,16 +13,18 @@
 // One workgroup of 256 threads, everything in LDS:
 //  1. nb[u] = ceil(len[u] / 64) and the exclusive prefix cx of the unit costs
 //     nb[u] + F (block-wide scan); quota = ceil(cx[U] / P) + F.
-//  2. The greedy walk, one part per iteration, on wavefront 0.  Write the
-//     cursor as a cost position s = cx[u0] + j0.  A part may spend up to
-//     lim = s + quota; it takes every following unit whole whose end fits,
-//     cx[u + 1] <= lim -- a run of units, since the costs are positive, counted
-//     with one ballot per 64 units -- and then cuts the next unit if more than
-//     F of the budget is left.  The next part starts at lim - F after a cut,
-//     else at the end of the last whole unit.
+//  2. The greedy walk on wavefront 0.  A part starting at block j0 of unit u0
+//     may spend up to lim = cx[u0] + j0 + quota.  If the unit's remaining
+//     blocks do not fit (nb - j0 + F > quota), the part and the ones after it
+//     each cut quota - F blocks of the unit until the rest fits; that run of
+//     parts is written at once.  Otherwise the part takes every unit whose end
+//     fits, cx[u + 1] <= lim -- a run of units, since the costs are positive,
+//     counted with one ballot per 64 units -- and then cuts the next unit if
+//     more than F of the budget is left.  At most 2 min(U, P) + 1 iterations.
 //  3. Per-part segment counts -> part_ptr (scan); per-unit segment counts and
 //     first part (LDS atomics) -> cumulative counts, slots and the split list
-//     (scans); then every part writes its segments in parallel.
+//     (scans); then every part writes its segments in parallel.  The scans are
+//     wavefront prefix sums combined across the four wavefronts.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -47,34 +49,50 @@ struct SchedDevParams {
   int32_t units, parts, topk, sparse, rows, row_blocks;
 };
 
+constexpr int kWaves = kThreads / 64;
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ int wave_max(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = max(x, __shfl_xor(x, d));
+  return x;
+}
+
 // Exclusive scan of a[0..n) in LDS, in place, by the whole block; returns the
-// total.  Each thread scans a contiguous run, the run totals are scanned by
-// thread 0.  Every thread of the block must call it.
+// total.  Each thread scans a contiguous run; the run totals are scanned
+// within each wavefront and then across the wavefronts.  Every thread of the
+// block must call it.
 __device__ int block_exclusive_scan(int* a, int n, int* tmp) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = min(n, t * per), hi = min(n, lo + per);
   int run = 0;
   for (int i = lo; i < hi; ++i) run += a[i];
-  tmp[t] = run;
+  const int incl = wave_inclusive_scan(run);
+  if (lane == 63) tmp[wave] = incl;
   __syncthreads();
-  if (t == 0) {
-    int acc = 0;
-    for (int i = 0; i < kThreads; ++i) {
-      const int v = tmp[i];
-      tmp[i] = acc;
-      acc += v;
-    }
-    tmp[kThreads] = acc;
+  int acc = incl - run, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = tmp[w];
+    if (w < wave) acc += v;
+    total += v;
   }
-  __syncthreads();
-  int acc = tmp[t];
   for (int i = lo; i < hi; ++i) {
     const int v = a[i];
     a[i] = acc;
     acc += v;
   }
-  const int total = tmp[kThreads];
   __syncthreads();
   return total;
 }
@@ -117,25 +135,44 @@ __global__ __launch_bounds__(kThreads) void mla_sched_dev(SchedDevParams p) {
   const int quota = (total + P - 1) / P + kOverhead;
   __syncthreads();
 
-  // 2. the walk (wavefront 0 only; all its branches are uniform)
+  // 2. the walk (wavefront 0 only; all its branches are uniform).  A part
+  // starting at block j0 of unit u0 whose remaining blocks do not fit in one
+  // part (nb - j0 + F > quota) takes just a cut of quota - F blocks, and so do
+  // the parts after it until the rest fits: such a run of parts inside one
+  // unit is written in one iteration.  Otherwise the part takes at least unit
+  // u0 whole, then possibly more units and a cut.
   if (t < 64 && !s_bad) {
     const int lane = t;
-    int u0 = 0, cxu0 = 0, s = 0, np = 0;
+    const int step = quota - kOverhead;  // blocks a fresh part cuts (quota > F)
+    int u0 = 0, cxu0 = 0, j0 = 0, np = 0;
     while (u0 < U && np < P) {
-      const int j0 = s - cxu0;
-      const int lim = s + quota;
+      const int lim = cxu0 + j0 + quota;
+      int v = u0 + 1 + lane <= U ? cx[u0 + 1 + lane] : INT_MAX;  // cx[u0 + 1 + lane]
+      const int nbu = __builtin_amdgcn_readfirstlane(v) - cxu0 - kOverhead;
+      if (nbu - j0 + kOverhead > quota) {
+        int k = (nbu + kOverhead - quota - j0 + step - 1) / step;
+        k = min(k, P - np);
+        for (int i = lane; i < k; i += 64) {
+          pu[np + i] = u0;
+          pj[np + i] = j0 + i * step;
+          pcnt[np + i] = 0;
+          pcut[np + i] = step;
+          pseg[np + i] = 1;
+        }
+        np += k;
+        j0 += k * step;
+        continue;
+      }
       int count = 0, cx_un = cxu0;
-      for (int c0 = u0 + 1; c0 <= U; c0 += 64) {
-        const int i = c0 + lane;
-        const int v = i <= U ? cx[i] : INT_MAX;
+      for (int c0 = u0 + 1;; c0 += 64) {
+        if (c0 != u0 + 1) v = c0 + lane <= U ? cx[c0 + lane] : INT_MAX;
         const int k = __popcll(__ballot(v <= lim));
         if (k > 0) cx_un = __builtin_amdgcn_readlane(v, k - 1);
         count += k;
-        if (k < 64) break;
+        if (k < 64 || c0 + 64 > U) break;
       }
-      const int un = u0 + count;
-      const int jn = count == 0 ? j0 : 0;
-      const int rem = lim - cx_un - jn;
+      const int un = u0 + count;  // count >= 1
+      const int rem = lim - cx_un;
       const int cut = (un < U && rem > kOverhead) ? rem - kOverhead : 0;
       if (lane == 0) {
         pu[np] = u0;
@@ -146,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_dev(SchedDevParams p) {
       }
       u0 = un;
       cxu0 = cx_un;
-      s = cx_un + jn + cut;
+      j0 = cut;
       ++np;
     }
     if (lane == 0) {
@@ -179,15 +216,12 @@ __global__ __launch_bounds__(kThreads) void mla_sched_dev(SchedDevParams p) {
     uidx[u] = ucnt[u] >= 2 ? 1 : 0;
     mx = max(mx, ucnt[u]);
   }
-  tmp[t] = mx;
+  mx = wave_max(mx);
+  if ((t & 63) == 0) tmp[t >> 6] = mx;
   __syncthreads();
-  if (t == 0) {
-    int m = 0;
-    for (int i = 0; i < kThreads; ++i) m = max(m, tmp[i]);
-    tmp[kThreads] = m;
-  }
-  __syncthreads();
-  const int max_splits = tmp[kThreads];
+  int max_splits = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) max_splits = max(max_splits, tmp[w]);
   __syncthreads();
 
   const int off_segs = kMetaHeaderInts + NP + 1;
