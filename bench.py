@@ -14,9 +14,10 @@ the previous step.
 
 Algorithmic work (what the method must do, not padded work):
   FLOP  = sum over (query row, visible key) of 2 * (d_qk + d_v)
-  bytes = every visible cache row once per request (d_qk * 2 B; the value is
-          inside it) + q, O (bf16) and LSE (fp32) of the computed heads
-          + block-table entries (or indices) read + sequence lengths.
+  bytes = every visible cache row once per request (d_qk * 2 B, or 656 B for
+          an FP8-with-scale row; the value is inside it) + q, O (bf16) and LSE
+          (fp32) of the computed heads + block-table entries (or indices) read
+          + sequence lengths.
 The split workspace traffic is overhead and is not counted.
 
 Prints one JSON line.  The step time is the whole decode (split-KV then
@@ -55,13 +56,14 @@ def algorithmic_work(case) -> dict:
     """Integer accounting of the work the method must do (see module docstring)."""
     s_q, d_qk, d_v = case["s_q"], case["d_qk"], case["d_v"]
     B = case["q"].shape[0]
+    row_bytes = 656 if case.get("kv_fp8") else d_qk * 2
     if case["sparse"]:
         heads = case["active_h_q"]
         idx = case["indices"]
         nrows = case["kvcache"].shape[0] * case["kvcache"].shape[1]
         valid = ((idx >= 0) & (idx < nrows)).sum().item()
         flop = valid * heads * 2 * (d_qk + d_v)
-        kv_bytes = valid * d_qk * 2
+        kv_bytes = valid * row_bytes
         meta_bytes = idx.numel() * 4
         keys = valid
     else:
@@ -72,7 +74,7 @@ def algorithmic_work(case) -> dict:
             for i in range(s_q):
                 keys += max(0, min(L, L - s_q + i + 1)) if case["causal"] else L
         flop = keys * heads * 2 * (d_qk + d_v)
-        kv_bytes = sum(sl) * d_qk * 2
+        kv_bytes = sum(sl) * row_bytes
         meta_bytes = sum((L + 63) // 64 for L in sl) * 4 + B * 4
     q_bytes = B * s_q * heads * d_qk * 2
     o_bytes = B * s_q * heads * (d_v * 2 + 4)
@@ -126,7 +128,7 @@ def copy_probe(torch, dev, reps: int = 3):
     del src, dst
 
 
-def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600,
+def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
                    probe: bool = False) -> dict:
     import torch
 
@@ -138,7 +140,7 @@ def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600,
     dev = torch.device("cuda", 0)
     q = case["q"].to(dev)
     kv0 = case["kvcache"].to(dev)
-    pool_mb = kv0.numel() * 2 / 2**20
+    pool_mb = kv0.numel() * kv0.element_size() / 2**20
     copies = max(1, min(8, math.ceil(rotate_mb / max(pool_mb, 1e-9))))
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     bt = case["block_table"].to(dev)
@@ -156,6 +158,22 @@ def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600,
         meta = get_meta()
     torch.cuda.synchronize()
     metadata_us = (time.perf_counter() - t0) / 20 * 1e6
+
+    # the same schedule built on the device (one single-workgroup kernel)
+    if case["sparse"]:
+        dmeta = lambda: mla.mla_get_metadata_device(  # noqa: E731
+            None, case["s_q"], case["h_q"], topk=case["topk"], active_h_q=case["active_h_q"],
+            batch=int(case["q"].shape[0]), device=dev)
+    else:
+        dmeta = lambda: mla.mla_get_metadata_device(sl, case["s_q"], case["h_q"])  # noqa: E731
+    dmeta()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        dmeta()
+    e1.record()
+    torch.cuda.synchronize()
+    metadata_device_us = e0.elapsed_time(e1) / 20 * 1e3
 
     B, s_q, h_q = case["q"].shape[:3]
     out = torch.empty((B, s_q, h_q, case["d_v"]), dtype=torch.bfloat16, device=dev)
@@ -232,7 +250,7 @@ def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600,
         case=case, work=work, ms_step=ms_step, split_ms=split_ms, combine_ms=comb_ms,
         tflops=work["flop"] / (ms_step * 1e-3) / 1e12,
         gbs=work["bytes"] / (ms_step * 1e-3) / 1e9,
-        metadata_us=metadata_us, ms_with_meta=ms_with_meta,
+        metadata_us=metadata_us, metadata_device_us=metadata_device_us, ms_with_meta=ms_with_meta,
         roofline=dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
                       frac=round(achieved / peak, 4), traffic=None),
         sched=dict(num_parts=meta.num_parts, row_blocks=meta.row_blocks,
@@ -243,11 +261,11 @@ def bench_workload(k: int, steps: int, warmup: int, rotate_mb: int = 600,
     return res
 
 
-def traffic_path(k: int) -> str:
+def traffic_path(k) -> str:
     return os.path.join(ROOT, "profiles", f"splitkv_traffic_workload{k}.json")
 
 
-def load_traffic(k: int):
+def load_traffic(k):
     """HBM bytes per launch of the split-KV kernel from the committed counter
     summary of workload k, if it was taken on the current kernel source."""
     path = traffic_path(k)
@@ -302,7 +320,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="seeded workload (2 = varlen decode, h_q=128: the headline)")
-    ap.add_argument("--others", default="3,4,5",
+    ap.add_argument("--others", default="3,4,5,4f,5f",
                     help="extra workloads timed into 'other_workloads' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -353,6 +371,7 @@ def main():
         "frac_hbm_peak": round(r["gbs"] / PEAK_HBM_GBS, 4),
         "kernels_ms": {"splitkv": round(r["split_ms"], 5), "combine": round(r["combine_ms"], 5)},
         "metadata_us": round(r["metadata_us"], 1),
+        "metadata_device_us": round(r["metadata_device_us"], 1),
         "with_metadata": {"ms_per_step": round(r["ms_with_meta"], 5),
                           "tflops": round(r["work"]["flop"] / (r["ms_with_meta"] * 1e-3) / 1e12, 3)},
         "schedule": r["sched"],
@@ -362,8 +381,8 @@ def main():
         "kernel_source_hash": kernel_hash(),
     }
     others = {}
-    for k in [int(x) for x in args.others.split(",") if x.strip()]:
-        if k == args.workload:
+    for k in [x.strip() for x in args.others.split(",") if x.strip()]:
+        if k == str(args.workload):
             continue
         o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2))
         o["roofline"]["traffic"] = load_traffic(k)
@@ -373,6 +392,8 @@ def main():
             "frac_mfma_peak": round(o["tflops"] / PEAK_BF16_TFLOPS, 4),
             "frac_hbm_peak": round(o["gbs"] / PEAK_HBM_GBS, 4),
             "kernels_ms": {"splitkv": round(o["split_ms"], 5), "combine": round(o["combine_ms"], 5)},
+            "metadata_device_us": round(o["metadata_device_us"], 1),
+            "kv_format": "fp8 with scale (656 B/row)" if o["case"].get("kv_fp8") else "bf16",
             "roofline": o["roofline"], "schedule": o["sched"],
         }
         del o

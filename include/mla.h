@@ -267,6 +267,55 @@ int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t bat
                 int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
                 size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * FP8 KV cache ("FP8 with scale": upstream FlashMLA README, "FP8 KV Cache";
+ * the pages' is_fp8_kvcache flag).  Every cache row is 656 bytes:
+ *   bytes   0..511  512 float8 e4m3 values (OCP E4M3FN: bias 7, no infinity,
+ *                   S.1111.111 is NaN) -- the NoPE part,
+ *   bytes 512..527  4 fp32 scales; scale g applies to values 128g..128g+127,
+ *   bytes 528..655  64 bf16 values -- the RoPE part, not quantized.
+ * The kernel dequantizes each NoPE value to bf16 as bf16(fp32(v) * scale)
+ * (the product rounded to fp32, then to bf16, to nearest even), keeps the
+ * RoPE values, and computes exactly as for a bf16 cache whose rows are these
+ * 576 values (V = the first 512).  q, out and lse are as for bf16.
+ *
+ * Same arguments and checks as the bf16 entry points, except:
+ *   kvcache   [num_blocks, page_block_size, h_kv, 656] bytes, device,
+ *             16-byte aligned (rows are 16-byte aligned since 656 = 41 * 16).
+ *   d_qk      must be 576 (MLA_E_NOTSUP otherwise), d_v 512.
+ * The metadata and workspace are the same as for a bf16 cache.
+ */
+int mla_decode_paged_fp8(const void* q, const void* kvcache, const int32_t* block_table,
+                         const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                         int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                         int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                         float softmax_scale, const int32_t* meta_dev,
+                         const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                         void* out, float* lse, void* stream);
+
+int mla_decode_sparse_fp8(const void* q, const void* kvcache, const int32_t* indices,
+                          int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                          int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                          float softmax_scale, const int32_t* meta_dev,
+                          const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, void* stream);
+
+/* The split-KV stage alone for an FP8 cache (then mla_combine), as above. */
+int mla_splitkv_paged_fp8(const void* q, const void* kvcache, const int32_t* block_table,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                          int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                          int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                          float softmax_scale, const int32_t* meta_dev,
+                          const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, void* stream);
+
+int mla_splitkv_sparse_fp8(const void* q, const void* kvcache, const int32_t* indices,
+                           int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                           int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                           float softmax_scale, const int32_t* meta_dev,
+                           const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                           void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

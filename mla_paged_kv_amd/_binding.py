@@ -77,6 +77,12 @@ def _load():
     lib.mla_splitkv_paged.argtypes = lib.mla_decode_paged.argtypes
     lib.mla_splitkv_sparse.restype = ctypes.c_int
     lib.mla_splitkv_sparse.argtypes = lib.mla_decode_sparse.argtypes
+    for name in ("mla_decode_paged_fp8", "mla_splitkv_paged_fp8"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = lib.mla_decode_paged.argtypes
+    for name in ("mla_decode_sparse_fp8", "mla_splitkv_sparse_fp8"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = lib.mla_decode_sparse.argtypes
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [vp, pinfo, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
     _lib = lib
@@ -257,6 +263,21 @@ def _prep_outputs(q, meta, dv, workspace, out, lse):
     return out, lse, workspace, ws_bytes
 
 
+FP8_ROW_BYTES = 656  # "FP8 with scale" cache row: 512 e4m3, 4 fp32 scales, 64 bf16
+
+
+def _kv_format(q, kvcache):
+    """'bf16' or 'fp8' (uint8 rows of 656 bytes, d_qk must be 576)."""
+    if kvcache.dtype == torch.uint8:
+        _need(kvcache.shape[-1] == FP8_ROW_BYTES, "an FP8 cache has 656-byte rows")
+        _need(q.shape[-1] == 576, "the FP8 cache format needs d_qk = 576")
+        return "fp8"
+    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16,
+          "q and kvcache must be bf16 (or kvcache uint8 FP8-with-scale rows)")
+    _need(kvcache.shape[-1] == q.shape[-1], "kvcache row width must equal q's d_qk")
+    return "bf16"
+
+
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -269,9 +290,13 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
     ``stage="split"`` runs only the split-KV kernel (then call
     :func:`mla_combine` with the same workspace, out and lse)."""
     lib = _load()
-    fn = lib.mla_decode_paged if stage == "all" else lib.mla_splitkv_paged
     _need(q.dim() == 4 and kvcache.dim() == 4, "q is [B, s_q, h_q, d_qk], kvcache [blocks, 64, h_kv, d_qk]")
-    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
+    _need(q.dtype == torch.bfloat16, "q must be bf16")
+    fp8 = _kv_format(q, kvcache) == "fp8"
+    if fp8:
+        fn = lib.mla_decode_paged_fp8 if stage == "all" else lib.mla_splitkv_paged_fp8
+    else:
+        fn = lib.mla_decode_paged if stage == "all" else lib.mla_splitkv_paged
     _need(q.is_cuda and kvcache.is_cuda and block_table.is_cuda and cache_seqlens.is_cuda,
           "all tensors must be on the GPU")
     _need(q.is_contiguous() and kvcache.is_contiguous() and block_table.is_contiguous()
@@ -280,8 +305,7 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
           "block_table and cache_seqlens must be int32")
     _need(not meta.sparse, "metadata was built for sparse decode")
     B, s_q, h_q, d_qk = q.shape
-    nblk, page, h_kv, d_kv = kvcache.shape
-    _need(d_kv == d_qk, "kvcache row width must equal q's d_qk")
+    nblk, page, h_kv, _ = kvcache.shape
     _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
     _need(cache_seqlens.shape == (B,), "cache_seqlens must be [B]")
     if not meta.device_built:  # (device metadata is not read back: no synchronisation)
@@ -307,17 +331,20 @@ def mla_decode_sparse(q, kvcache, indices, dv: int, meta: Metadata,
                       stage: str = "all"):
     """Top-k sparse decode; heads past the metadata's active count are not written."""
     lib = _load()
-    fn = lib.mla_decode_sparse if stage == "all" else lib.mla_splitkv_sparse
     _need(q.dim() == 4 and kvcache.dim() == 4 and indices.dim() == 3, "bad ranks")
-    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
+    _need(q.dtype == torch.bfloat16, "q must be bf16")
+    fp8 = _kv_format(q, kvcache) == "fp8"
+    if fp8:
+        fn = lib.mla_decode_sparse_fp8 if stage == "all" else lib.mla_splitkv_sparse_fp8
+    else:
+        fn = lib.mla_decode_sparse if stage == "all" else lib.mla_splitkv_sparse
     _need(indices.dtype == torch.int32, "indices must be int32")
     _need(q.is_cuda and kvcache.is_cuda and indices.is_cuda, "all tensors must be on the GPU")
     _need(q.is_contiguous() and kvcache.is_contiguous() and indices.is_contiguous(),
           "tensors must be contiguous")
     _need(meta.sparse, "metadata was built for dense decode")
     B, s_q, h_q, d_qk = q.shape
-    nblk, page, h_kv, d_kv = kvcache.shape
-    _need(d_kv == d_qk, "kvcache row width must equal q's d_qk")
+    nblk, page, h_kv, _ = kvcache.shape
     _need(indices.shape[:2] == (B, s_q), "indices must be [B, s_q, topk]")
     topk = indices.shape[2]
     _need(topk == meta.topk, f"indices topk {topk} != metadata topk {meta.topk}")
@@ -356,8 +383,7 @@ def get_mla_metadata(cache_seqlens, num_q_tokens_per_head_k: int, num_heads_k: i
     Returns ``(tile_scheduler_metadata, num_splits)``: the :class:`Metadata`
     object (pass it back as ``tile_scheduler_metadata``) and the cumulative
     per-unit segment counts on the device."""
-    if is_fp8_kvcache:
-        raise NotImplementedError("FP8 KV cache is not built; the cache must be bf16")
+    # (the schedule does not depend on the cache format)
     rows = int(num_q_tokens_per_head_k)
     if topk:
         _need(num_heads_q is not None, "sparse metadata needs num_heads_q")
@@ -378,7 +404,11 @@ def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v: i
                            is_fp8_kvcache: bool = False, indices=None):
     """The pages' ``flash_mla_with_kvcache``; returns (out, lse)."""
     if is_fp8_kvcache:
-        raise NotImplementedError("FP8 KV cache is not built; the cache must be bf16")
+        if k_cache.dtype != torch.uint8:  # e.g. a float8 view of the same bytes
+            k_cache = k_cache.view(torch.uint8)
+        _need(k_cache.shape[-1] == FP8_ROW_BYTES, "is_fp8_kvcache: rows must be 656 bytes")
+    else:
+        _need(k_cache.dtype == torch.bfloat16, "the cache must be bf16 unless is_fp8_kvcache")
     if indices is not None:
         return mla_decode_sparse(q, k_cache, indices, head_dim_v, tile_scheduler_metadata,
                                  softmax_scale=softmax_scale)

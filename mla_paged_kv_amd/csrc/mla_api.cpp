@@ -29,7 +29,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q, int32_t h_q,
                  int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
                  int32_t page_block_size, const int32_t* meta_dev, const mla_sched_info* info,
-                 void* workspace, size_t workspace_bytes, void* out, float* lse) {
+                 void* workspace, size_t workspace_bytes, void* out, float* lse, bool fp8) {
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || d_qk < 1 || dv < 1 || num_blocks < 0 ||
       page_block_size < 1)
     return set_error(MLA_E_INVAL, "decode: negative or zero shape");
@@ -37,6 +37,8 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
   if (page_block_size != kPage)
     return set_error(MLA_E_NOTSUP, "decode: page_block_size=%d (only 64)", page_block_size);
   if (d_qk != 576 && d_qk != 512) return set_error(MLA_E_NOTSUP, "decode: d_qk=%d", d_qk);
+  if (fp8 && d_qk != 576)
+    return set_error(MLA_E_NOTSUP, "decode: the FP8 cache format needs d_qk=576, got %d", d_qk);
   if (dv > d_qk) return set_error(MLA_E_INVAL, "decode: dv=%d > d_qk=%d", dv, d_qk);
   if (dv != kDV) return set_error(MLA_E_NOTSUP, "decode: dv=%d (only 512)", dv);
   if (info == nullptr) return set_error(MLA_E_INVAL, "decode: null info");
@@ -108,15 +110,15 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
   return MLA_OK;
 }
 
-int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, void* workspace,
-           int32_t dv, void* stream, int stages) {
+int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, bool fp8,
+           void* workspace, int32_t dv, void* stream, int stages) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   carve_workspace(info, workspace, dv, &kp.ws_o, &kp.ws_lse);
   kp.num_parts = info->num_parts;
   kp.row_blocks = info->row_blocks;
   kp.rows = info->rows;
   if (stages & kStageSplit) {
-    const hipError_t e = launch_splitkv(kp, d_qk, sparse, st);
+    const hipError_t e = launch_splitkv(kp, d_qk, sparse, fp8, st);
     if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
   if (stages & kStageCombine)
@@ -174,10 +176,10 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
                       int32_t page_block_size, int32_t bt_stride, int32_t causal,
                       float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
                       void* workspace, size_t workspace_bytes, void* out, float* lse,
-                      void* stream, int stages) {
+                      void* stream, int stages, bool fp8) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
-                        meta_dev, info, workspace, workspace_bytes, out, lse);
+                        meta_dev, info, workspace, workspace_bytes, out, lse, fp8);
   if (rc != MLA_OK || batch == 0) return rc;
   if (!block_table || !cache_seqlens) return set_error(MLA_E_INVAL, "decode_paged: null block_table/seqlens");
   if (bt_stride < 1) return set_error(MLA_E_INVAL, "decode_paged: bt_stride=%d", bt_stride);
@@ -209,7 +211,7 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
   kp.topk = 0;
   kp.causal = causal;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, false, workspace, dv, stream, stages);
+  return launch(kp, info, d_qk, false, fp8, workspace, dv, stream, stages);
 }
 
 int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indices,
@@ -217,10 +219,10 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
                        int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
                        float softmax_scale, const int32_t* meta_dev,
                        const mla_sched_info* info, void* workspace, size_t workspace_bytes,
-                       void* out, float* lse, void* stream, int stages) {
+                       void* out, float* lse, void* stream, int stages, bool fp8) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
-                        meta_dev, info, workspace, workspace_bytes, out, lse);
+                        meta_dev, info, workspace, workspace_bytes, out, lse, fp8);
   if (rc != MLA_OK || batch == 0) return rc;
   if (!indices) return set_error(MLA_E_INVAL, "decode_sparse: null indices");
   if (topk < 1) return set_error(MLA_E_INVAL, "decode_sparse: topk=%d", topk);
@@ -249,7 +251,7 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
   kp.topk = topk;
   kp.causal = 0;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, true, workspace, dv, stream, stages);
+  return launch(kp, info, d_qk, true, fp8, workspace, dv, stream, stages);
 }
 
 }  // namespace mla
@@ -277,19 +279,35 @@ extern "C" {
       softmax_scale, meta_dev, info, workspace, workspace_bytes, out, lse, stream
 
 int mla_decode_paged(MLA_PAGED_ARGS) {
-  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine);
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, false);
 }
 
 int mla_splitkv_paged(MLA_PAGED_ARGS) {
-  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit);
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, false);
 }
 
 int mla_decode_sparse(MLA_SPARSE_ARGS) {
-  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine);
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, false);
 }
 
 int mla_splitkv_sparse(MLA_SPARSE_ARGS) {
-  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit);
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, false);
+}
+
+int mla_decode_paged_fp8(MLA_PAGED_ARGS) {
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, true);
+}
+
+int mla_splitkv_paged_fp8(MLA_PAGED_ARGS) {
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, true);
+}
+
+int mla_decode_sparse_fp8(MLA_SPARSE_ARGS) {
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, true);
+}
+
+int mla_splitkv_sparse_fp8(MLA_SPARSE_ARGS) {
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, true);
 }
 
 int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,

@@ -8,10 +8,13 @@
 namespace mla {
 
 constexpr int kMetaHeaderInts = 16;  // int32 header ahead of part_ptr in the metadata
+// "FP8 with scale" cache row: 512 e4m3 values, 4 fp32 scales (one per 128
+// values), 64 bf16 RoPE values (upstream FlashMLA README, "FP8 KV Cache").
+constexpr int kFp8RowBytes = 656;
 
 struct SplitKVParams {
   const uint16_t* q;           // [batch, s_q, h_q, d_qk] bf16
-  const uint16_t* kv;          // [num_blocks * 64, d_qk] bf16 (h_kv = 1)
+  const uint16_t* kv;          // [num_blocks * 64] rows: d_qk bf16, or 656-byte FP8 rows (h_kv = 1)
   const int32_t* block_table;  // dense: [batch, bt_stride]
   const int32_t* seqlens;      // dense: [batch]
   const int32_t* indices;      // sparse: [batch * s_q, topk]
@@ -43,7 +46,8 @@ struct CombineParams {
   int32_t sparse;
 };
 
-hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream);
+hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, bool fp8,
+                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace mla

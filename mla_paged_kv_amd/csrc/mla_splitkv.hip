@@ -56,6 +56,10 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Read-only metadata (scheduler output, block table, sequence lengths) is
@@ -172,7 +176,10 @@ struct Gather {
 
 // WIDE (sparse only): the cache pool is 4 GiB or larger, so rows are reached
 // with 64-bit addresses instead of 32-bit offsets into one buffer resource.
-template <int D_QK, bool SPARSE, bool WIDE>
+// FP8 (D_QK = 576 only): the cache holds 656-byte "FP8 with scale" rows, which
+// are staged in LDS as they are and dequantized to the bf16 tile layout
+// before the tile is computed.
+template <int D_QK, bool SPARSE, bool WIDE, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_splitkv(SplitKVParams p) {
   // The body is compiled for the GPU only; the host pass needs just the
@@ -191,11 +198,21 @@ void mla_splitkv(SplitKVParams p) {
   constexpr int NVB = FMAX / 4;           // V-read bases (ct mod NVB)
   static_assert(NLD % kWaves == 0 && (16 * CPR) % 64 == 0, "16 whole rows per wavefront");
   static_assert(2 * NLW <= KK + 1, "gather slices fit the QK loop");
+  static_assert(!FP8 || D_QK == 576, "the FP8 row format carries 512 + 64 values");
+  constexpr int SROW = kFp8RowBytes;      // FP8 cache row: 512 e4m3, 4 fp32 scales, 64 bf16
+  constexpr int SBUF = kPage * SROW;      // staged FP8 tile (41 KB)
+  constexpr int SNL = SBUF / 1024;        // 1 KB gather loads per FP8 tile (41)
+  static_assert(SBUF % 1024 == 0, "whole 1 KB loads");
+  // bf16 tiles: two buffers, the next tile streams into one while the other is
+  // computed.  FP8 tiles: the raw rows stream into two staging buffers and
+  // one bf16 buffer holds the dequantized tile being computed; the pair
+  // exchange area then lives in the staging buffer just dequantized.
+  constexpr int XP_BYTES = kWaves * 2 * 64 * 16, XM_BYTES = kWaves * 32 * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t buf_a[BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf_b[BUF];
-  __shared__ __attribute__((aligned(16))) s16x8 x_p[kWaves][2][64];       // bf16 P of a pair half
-  __shared__ float x_max[kWaves][32];                                      // row maxima of a half
-  __shared__ float x_sum[kWaves][32];                                      // row sums of a half
+  __shared__ __attribute__((aligned(1024))) uint8_t buf_b[FP8 ? 16 : BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t stg_a[FP8 ? SBUF : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t stg_b[FP8 ? SBUF : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t x_own[FP8 ? 16 : XP_BYTES + 2 * XM_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
@@ -295,15 +312,16 @@ void mla_splitkv(SplitKVParams p) {
   // contributes exactly zero), and an invalid sparse index is replaced by the
   // tile's first valid one (also masked).  A sparse tile without any valid
   // index is neither loaded nor computed.
+  constexpr int ROWB = FP8 ? SROW : RSB;  // bytes of one cache row in memory
   auto page_rsrc = [&](int phys) __attribute__((always_inline)) {
-    const uint8_t* pg = reinterpret_cast<const uint8_t*>(p.kv) + size_t(phys) * kPage * D_QK * 2;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, kPage * D_QK * 2,
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>(p.kv) + size_t(phys) * kPage * ROWB;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, kPage * ROWB,
                                             kBufferWord3);
   };
   // the whole pool (sparse rows, pools below 4 GiB)
   auto pool_rsrc = [&]() __attribute__((always_inline)) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), 0,
-                                            int(uint32_t(p.num_rows) * uint32_t(RSB)), kBufferWord3);
+                                            int(uint32_t(p.num_rows) * uint32_t(ROWB)), kBufferWord3);
   };
   auto plan_gather = [&](int blk, const TileMeta& m) __attribute__((always_inline)) -> Gather {
     Gather g;
@@ -359,6 +377,98 @@ void mla_splitkv(SplitKVParams p) {
   auto gather_all = [&](const Gather& g, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NLW; ++i) gather_one(g, dst, i, lane);
+  };
+  // FP8 tile: the 64 raw rows, back to back, in 41 loads of 1 KB; wavefront w
+  // issues loads w, w + 4, ...  Lane chunk q of the tile is chunk q % 41 of
+  // tile row q / 41.  Rows are clamped / substituted as for bf16 tiles.  The
+  // lane id goes through an opaque copy so the per-lane offsets are
+  // recomputed for every tile rather than kept live (or spilled) across it.
+  auto gather_fp8 = [&](const Gather& g, uint8_t* dst) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < (SNL + kWaves - 1) / kWaves; ++i) {
+      const int n = wave + kWaves * i;
+      if (n < SNL) {
+        const int q = 64 * n + ln;
+        int t = q / (SROW / 16);
+        const int cb = 16 * (q - t * (SROW / 16));  // byte of the chunk in its row
+        lds_void* to = (lds_void*)(dst + n * 1024);
+        if constexpr (SPARSE) {
+          const int r = __shfl(g.idx, t);
+          if constexpr (WIDE) {
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * SROW + cb;
+            __builtin_amdgcn_global_load_lds(src, to, 16, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), to, 16, r * SROW + cb, 0, 0, 0);
+          }
+        } else {
+          if (t > g.tmax) t = g.tmax;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(g.phys), to, 16, t * SROW + cb, 0, 0,
+                                                  0);
+        }
+      }
+    }
+  };
+  // Dequantizes a staged FP8 tile into the bf16 tile layout (upstream
+  // FlashMLA README, "FP8 KV Cache": value * scale of its group of 128, then
+  // bf16; the RoPE part is bf16 already).  Wavefront w takes tile rows
+  // w, w + 4, ..., and lane l makes bf16 chunk l of the row from 8 e4m3
+  // values (scale group l / 16): 16 lanes read one contiguous 128 bytes and
+  // write 8 distinct chunks of a swizzle group, so neither side conflicts.
+  // The product is rounded to fp32, then to bf16 (nearest even).
+  auto dequant = [&](const uint8_t* stg, uint8_t* dst) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed per tile (see gather_fp8)
+    const int fw = 4 * ((wave >> 1) & 1);  // swizzle bit of row w + 4i from the wave
+    const uint8_t* src = stg + wave * SROW;
+    uint8_t* drow = dst + wave * RSB;
+    // rows in groups of 4; the reads of group g + 1 are in flight while
+    // group g is converted
+    constexpr int GR = 4, NG = kPage / kWaves / GR;
+    u32x2 raw[2][GR];
+    float sc[2][GR];
+    auto read_group = [&](int g) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < GR; ++r) {
+        const uint8_t* sr = src + 4 * (GR * g + r) * SROW;
+        raw[g & 1][r] = *reinterpret_cast<const u32x2*>(sr + 8 * ln);
+        sc[g & 1][r] = *reinterpret_cast<const float*>(sr + 512 + 4 * (ln >> 4));
+      }
+    };
+    read_group(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) read_group(g + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < GR; ++r) {
+        const int i = GR * g + r;
+        const int f = fw + (i & 3);  // swz<72>(wave + 4 i)
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const u32x2 x = raw[g & 1][r];
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(x[e], false) * sc[g & 1][r];
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(x[e], true) * sc[g & 1][r];
+          w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+          w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+        }
+        *reinterpret_cast<u32x4*>(drow + 4 * i * RSB + 16 * (ln ^ f)) =
+            u32x4{w[0], w[1], w[2], w[3]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // RoPE: 8 chunks per row, 8 rows per pass (rows w + 4 (8 k + ln / 8))
+#pragma unroll
+    for (int k = 0; k < kPage / kWaves / 8; ++k) {
+      const int i = 8 * k + (ln >> 3);
+      const int c = ln & 7;
+      const int f = fw + (i & 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * i * SROW + 528 + 16 * c);
+      *reinterpret_cast<u32x4*>(drow + 4 * i * RSB + 16 * ((64 + c) ^ f)) = v;
+    }
   };
 
   // ---- per-segment state ----
@@ -447,8 +557,16 @@ void mla_splitkv(SplitKVParams p) {
   // queries are loaded once the QK product no longer needs the current ones.
   // gather_slice(i) issues slice i of the next tile's gather (between QK
   // k-steps).
-  auto compute_tile = [&](const uint8_t* buf, int blk, uint64_t vmask,
-                          int next_q_unit) __attribute__((always_inline)) {
+  // `xb`: the LDS area of the pair exchanges (P halves, row maxima and sums).
+  auto compute_tile = [&](const uint8_t* buf, int blk, uint64_t vmask, int next_q_unit,
+                          uint8_t* xb) __attribute__((always_inline)) {
+    s16x8* x_p = reinterpret_cast<s16x8*>(xb);                     // [wave][2][64]
+    float* x_max = reinterpret_cast<float*>(xb + XP_BYTES);           // [wave][32]
+    float* x_sum = reinterpret_cast<float*>(xb + XP_BYTES + XM_BYTES);  // [wave][32]
+    // FP8: the exchange area moves between the two staging buffers, so its
+    // lane offsets are recomputed per tile rather than kept live for both
+    int xl = lane;
+    if constexpr (FP8) asm volatile("" : "+v"(xl));
     // S^T of this half's 32 tokens as two accumulation chains (even and odd
     // k-steps), added at the end
     constexpr int QD = 4;  // K fragments prefetched this many k-steps ahead
@@ -468,7 +586,8 @@ void mla_splitkv(SplitKVParams p) {
       const int c = kk & 1;
       st[c] = mfma(kf[kk % (QD + 1)], qf[kk], kk < 2 ? f32x16{} : st[c]);
       // the next tile's gather, one slice every other k-step
-      if ((kk & 1) == 0 && kk / 2 < NLW) gather_slice(kk / 2);
+      if constexpr (!FP8)
+        if ((kk & 1) == 0 && kk / 2 < NLW) gather_slice(kk / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     st[0] += st[1];
@@ -520,9 +639,9 @@ void mla_splitkv(SplitKVParams p) {
       }
     }
     mloc = xor32_max(mloc);
-    if (lane < 32) x_max[wave][lane] = mloc;  // maximum over both token halves
+    if (lane < 32) x_max[32 * wave + xl] = mloc;  // maximum over both token halves
     lds_barrier();
-    mloc = fmaxf(mloc, x_max[wave ^ 1][lane & 31]) * p.scale_log2;
+    mloc = fmaxf(mloc, x_max[32 * (wave ^ 1) + (xl & 31)]) * p.scale_log2;
     const bool grow = mloc > m_run + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? mloc : m_run;
@@ -553,14 +672,14 @@ void mla_splitkv(SplitKVParams p) {
     }
     // exchange P halves and row sums with the pair partner
     const float own = xor32_sum(psum);
-    x_p[wave][0][lane] = pk[0];
-    x_p[wave][1][lane] = pk[1];
-    if (lane < 32) x_sum[wave][lane] = own;
+    x_p[128 * wave + xl] = pk[0];
+    x_p[128 * wave + 64 + xl] = pk[1];
+    if (lane < 32) x_sum[32 * wave + xl] = own;
     lds_barrier();
     s16x8 pp[2];
-    pp[0] = x_p[wave ^ 1][0][lane];
-    pp[1] = x_p[wave ^ 1][1][lane];
-    const float other = x_sum[wave ^ 1][lane & 31];
+    pp[0] = x_p[128 * (wave ^ 1) + xl];
+    pp[1] = x_p[128 * (wave ^ 1) + 64 + xl];
+    const float other = x_sum[32 * (wave ^ 1) + (xl & 31)];
     l_part += half == 0 ? own + other : other + own;  // same sum in both halves
     __builtin_amdgcn_sched_barrier(0);
 
@@ -639,7 +758,12 @@ void mla_splitkv(SplitKVParams p) {
     reset_state();
     const Gather g0 = plan_gather(ct.blk, m0);
     cmask = g0.vmask;
-    if (!SPARSE || cmask != 0) gather_all(g0, buf_a);
+    if (!SPARSE || cmask != 0) {
+      if constexpr (FP8)
+        gather_fp8(g0, stg_a);
+      else
+        gather_all(g0, buf_a);
+    }
   }
   // Tile j+1 is gathered during step j; metadata runs two tiles ahead of the
   // gathers (that of tile j+3 is read at the end of step j).  All scalar
@@ -656,7 +780,11 @@ void mla_splitkv(SplitKVParams p) {
   // `nxt_buf`.  The two buffers are distinct LDS objects named statically at
   // every call site, so the compiler can tell reads of one from the
   // asynchronous writes into the other and does not wait for those writes.
-  auto step = [&](const uint8_t* cur_buf, uint8_t* nxt_buf) __attribute__((always_inline)) -> bool {
+  // FP8: the buffers are the staging buffers; the next tile's gather is issued
+  // whole at the start of the step, then the current tile is dequantized into
+  // buf_a and computed, with the pair exchanges in its (consumed) staging
+  // buffer.
+  auto step = [&](uint8_t* cur_buf, uint8_t* nxt_buf) __attribute__((always_inline)) -> bool {
 #pragma unroll
     for (int ct_ = 0; ct_ < NCT; ++ct_) pin_agpr(acc[ct_]);  // loop-carried in AGPRs
     wait_vmem();
@@ -670,8 +798,17 @@ void mla_splitkv(SplitKVParams p) {
     nx_ln = lane;
     asm volatile("" : "+v"(nx_ln));
     const int next_q_unit = (ct.last && has_next) ? nt.u : -1;
-    if (!SPARSE || cmask != 0) {
-      compute_tile(cur_buf, ct.blk, cmask, next_q_unit);
+    if constexpr (FP8) {
+      if (has_next && (!SPARSE || nmask != 0)) gather_fp8(nx_plan, nxt_buf);
+      if (!SPARSE || cmask != 0) {
+        dequant(cur_buf, buf_a);
+        lds_barrier();
+        compute_tile(buf_a, ct.blk, cmask, next_q_unit, cur_buf);
+      } else if (next_q_unit >= 0) {
+        load_q(next_q_unit);
+      }
+    } else if (!SPARSE || cmask != 0) {
+      compute_tile(cur_buf, ct.blk, cmask, next_q_unit, x_own);
     } else {
       if (next_q_unit >= 0) load_q(next_q_unit);
 #pragma unroll
@@ -700,33 +837,44 @@ void mla_splitkv(SplitKVParams p) {
     n2meta = n3meta;
     return true;
   };
-  for (;;) {
-    if (!step(buf_a, buf_b)) break;
-    if (!step(buf_b, buf_a)) break;
+  if constexpr (FP8) {
+    for (;;) {
+      if (!step(stg_a, stg_b)) break;
+      if (!step(stg_b, stg_a)) break;
+    }
+  } else {
+    for (;;) {
+      if (!step(buf_a, buf_b)) break;
+      if (!step(buf_b, buf_a)) break;
+    }
   }
   wait_vmem();  // no load into LDS outlives the workgroup
 #endif
 }
 
-hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream) {
+hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, bool fp8,
+                          hipStream_t stream) {
   const int groups = p.num_parts * p.row_blocks;
   if (groups <= 0) return hipSuccess;
   const dim3 grid(groups), block(256);
   // sparse rows are addressed with 32-bit byte offsets while the pool fits
-  const bool wide = uint64_t(p.num_rows) * uint64_t(d_qk) * 2 > 0xFFFFFFFFull;
-#define MLA_LAUNCH(D)                                                                        \
+  const uint64_t row_bytes = fp8 ? kFp8RowBytes : uint64_t(d_qk) * 2;
+  const bool wide = uint64_t(p.num_rows) * row_bytes > 0xFFFFFFFFull;
+#define MLA_LAUNCH(D, F)                                                                     \
   do {                                                                                       \
     if (!sparse)                                                                             \
-      hipLaunchKernelGGL((mla_splitkv<D, false, false>), grid, block, 0, stream, p);         \
+      hipLaunchKernelGGL((mla_splitkv<D, false, false, F>), grid, block, 0, stream, p);      \
     else if (!wide)                                                                          \
-      hipLaunchKernelGGL((mla_splitkv<D, true, false>), grid, block, 0, stream, p);          \
+      hipLaunchKernelGGL((mla_splitkv<D, true, false, F>), grid, block, 0, stream, p);       \
     else                                                                                     \
-      hipLaunchKernelGGL((mla_splitkv<D, true, true>), grid, block, 0, stream, p);           \
+      hipLaunchKernelGGL((mla_splitkv<D, true, true, F>), grid, block, 0, stream, p);        \
   } while (0)
-  if (d_qk == 576)
-    MLA_LAUNCH(576);
+  if (fp8)
+    MLA_LAUNCH(576, true);
+  else if (d_qk == 576)
+    MLA_LAUNCH(576, false);
   else
-    MLA_LAUNCH(512);
+    MLA_LAUNCH(512, false);
 #undef MLA_LAUNCH
   return hipGetLastError();
 }

@@ -14,6 +14,12 @@ Recipe (shared by every config):
   workload, whose table is the whole permutation reshaped).
 * Sparse indices are ``block * 64 + offset`` of sorted distinct positions,
   with a tail of the sorted list replaced by -1.
+* FP8 caches ("FP8 with scale", 656-byte rows: 512 e4m3, 4 fp32 scales, 64
+  bf16): the row's 576 values are float32 standard normals (times 2^u per row,
+  u ~ U[-spread, spread], when asked); each group of 128 NoPE values gets the
+  scale amax / 448 (1 for an all-zero group) and is cast to float8_e4m3fn by
+  torch (nearest even); the 64 RoPE values are rounded to bfloat16.  This is
+  input preparation only -- the decode reads whatever bytes the cache holds.
 """
 from __future__ import annotations
 
@@ -44,6 +50,29 @@ def normal_bf16(rng: np.random.Generator, shape) -> torch.Tensor:
     return out.view(*shape)
 
 
+FP8_ROW = 656
+
+
+def fp8_rows(rng: np.random.Generator, n_rows: int, spread: float = 0.0) -> torch.Tensor:
+    """``n_rows`` FP8-with-scale cache rows as a uint8 tensor [n_rows, 656]."""
+    out = torch.empty((n_rows, FP8_ROW), dtype=torch.uint8)
+    per = max(1, CHUNK // 576)
+    for s in range(0, n_rows, per):
+        e = min(n_rows, s + per)
+        x = rng.standard_normal((e - s, 576), dtype=np.float32)
+        if spread:
+            x *= np.exp2(rng.uniform(-spread, spread, size=(e - s, 1))).astype(np.float32)
+        g = x[:, :512].reshape(e - s, 4, 128)
+        amax = np.abs(g).max(axis=2)
+        scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        codes = torch.from_numpy(np.ascontiguousarray(g / scale[:, :, None]).reshape(e - s, 512))
+        out[s:e, :512] = codes.to(torch.float8_e4m3fn).view(torch.uint8)
+        out[s:e, 512:528] = torch.from_numpy(scale.view(np.uint8).reshape(e - s, 16))
+        rope = bf16_from_f32(x[:, 512:]).view(torch.uint8).reshape(e - s, 128)
+        out[s:e, 528:] = rope
+    return out
+
+
 def _table_from_perm(perm: np.ndarray, nblocks: np.ndarray, width: int) -> np.ndarray:
     table = np.full((len(nblocks), width), -1, dtype=np.int32)
     cur = 0
@@ -56,8 +85,11 @@ def _table_from_perm(perm: np.ndarray, nblocks: np.ndarray, width: int) -> np.nd
 def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
                     seqlen_sampler=None, d_qk: int = 576, d_v: int = 512, h_kv: int = 1,
                     causal: bool = False, spare_frac: float = 0.0, table_width=None,
-                    reshape_table: bool = False, name: str = "dense") -> dict:
-    """A dense paged-decode case.  ``seqlens`` fixed, or drawn by ``seqlen_sampler(rng)``."""
+                    reshape_table: bool = False, name: str = "dense", kv_fp8: bool = False,
+                    fp8_spread: float = 0.0) -> dict:
+    """A dense paged-decode case.  ``seqlens`` fixed, or drawn by ``seqlen_sampler(rng)``.
+    ``kv_fp8``: the cache is FP8 with scale (d_qk must be 576)."""
+    assert not kv_fp8 or d_qk == 576
     rng = rng_for(seed)
     if seqlens is None:
         seqlens = np.asarray(seqlen_sampler(rng), dtype=np.int64)
@@ -77,9 +109,12 @@ def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
         perm = rng.permutation(pool).astype(np.int32)
         table = _table_from_perm(perm, nblocks, width)
     q = normal_bf16(rng, (B, s_q, h_q, d_qk))
-    kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
+    if kv_fp8:
+        kv = fp8_rows(rng, pool * PAGE * h_kv, fp8_spread).view(pool, PAGE, h_kv, FP8_ROW)
+    else:
+        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
     return dict(
-        name=name, sparse=False, q=q, kvcache=kv,
+        name=name, sparse=False, q=q, kvcache=kv, kv_fp8=kv_fp8,
         block_table=torch.from_numpy(table),
         cache_seqlens=torch.from_numpy(seqlens.astype(np.int32)),
         indices=None, s_q=s_q, h_q=h_q, h_kv=h_kv, d_qk=d_qk, d_v=d_v,
@@ -90,7 +125,8 @@ def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
 
 def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
                      topk: int, cache_len: int, invalid_tail: int, d_qk: int = 512,
-                     d_v: int = 512, h_kv: int = 1, name: str = "sparse") -> dict:
+                     d_v: int = 512, h_kv: int = 1, name: str = "sparse", kv_fp8: bool = False,
+                     fp8_spread: float = 0.0) -> dict:
     """A top-k sparse-decode case: every request owns ``cache_len`` tokens of a
     shared pool; each query token draws ``topk`` distinct positions, sorted,
     and the last ``invalid_tail`` entries become -1."""
@@ -99,8 +135,12 @@ def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
     pool = B * width
     perm = rng.permutation(pool).astype(np.int32)
     table = perm.reshape(B, width)
+    assert not kv_fp8 or d_qk == 576
     q = normal_bf16(rng, (B, s_q, h_q, d_qk))
-    kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
+    if kv_fp8:
+        kv = fp8_rows(rng, pool * PAGE * h_kv, fp8_spread).view(pool, PAGE, h_kv, FP8_ROW)
+    else:
+        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
     idx = np.empty((B, s_q, topk), dtype=np.int32)
     for b in range(B):
         for i in range(s_q):
@@ -110,7 +150,7 @@ def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
                 row[topk - invalid_tail:] = -1
             idx[b, i] = row
     return dict(
-        name=name, sparse=True, q=q, kvcache=kv,
+        name=name, sparse=True, q=q, kvcache=kv, kv_fp8=kv_fp8,
         block_table=torch.from_numpy(table.copy()),
         cache_seqlens=torch.full((B,), cache_len, dtype=torch.int32),
         indices=torch.from_numpy(idx), s_q=s_q, h_q=h_q, h_kv=h_kv, d_qk=d_qk,
@@ -149,14 +189,31 @@ CONFIGS = {
 }
 
 
-def make_config(k: int) -> dict:
-    """The five named workloads, seed 1000 + k."""
-    spec = dict(CONFIGS[k])
+# The same shapes with an FP8-with-scale cache (576-wide rows: the format holds
+# 512 + 64 values), seed 1000 + k as for the bf16 workload they follow.
+FP8_CONFIGS = {
+    "4f": dict(CONFIGS[4], name="skewed long context, FP8 cache: B=16 s_q=1 h_q=64, "
+                                "8 x logU[32k,128k] + 8 x U[1,256]", kv_fp8=True),
+    "5f": dict(CONFIGS[5], name="top-k sparse, FP8 cache: B=32 s_q=1 h_q=64 (16 active) "
+                                "d_qk=576 d_v=512 topk 2048, 102 invalid", d_qk=576, kv_fp8=True),
+}
+
+
+def make_config(k) -> dict:
+    """The five named workloads (k = 1..5), seed 1000 + k, and their FP8-cache
+    variants ("4f", "5f")."""
+    if isinstance(k, str) and k in FP8_CONFIGS:
+        spec = dict(FP8_CONFIGS[k])
+        seed = 1000 + int(k[:-1])
+    else:
+        k = int(k)
+        spec = dict(CONFIGS[k])
+        seed = 1000 + k
     kind = spec.pop("kind")
     name = spec.pop("name")
     if kind == "dense":
-        return make_dense_case(1000 + k, name=name, **spec)
-    return make_sparse_case(1000 + k, name=name, **spec)
+        return make_dense_case(seed, name=name, **spec)
+    return make_sparse_case(seed, name=name, **spec)
 
 
 def make_case(kind: str, seed: int, **kw) -> dict:
