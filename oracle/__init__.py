@@ -19,6 +19,9 @@ splits):
 * ``fp8.dequant_rows``   -- the "FP8 with scale" cache row (upstream README,
   "FP8 KV Cache"): both decode functions accept such a cache and dequantize
   the rows they read.
+* ``ref_sparse_prefill`` -- sparse MLA prefill (same README, "Sparse MLA
+  Prefill": out, max_logits and a base-2 LSE, in the order of its equivalent
+  PyTorch code).
 * ``ref_schedule``       -- the reference tile scheduler.  The pages give only
   its purpose (metadata from sequence lengths and the head configuration that
   spreads variable-length work over compute units); the algorithm is this
@@ -30,6 +33,7 @@ splits):
 """
 from . import fp8
 from .decode import ref_decode_paged, ref_decode_sparse, ref_attend_rows
+from .prefill import ref_sparse_prefill
 from .schedule import (ref_schedule, ref_num_parts, unpack_schedule,
                        SPLIT_OVERHEAD_BLOCKS, PAGE_BLOCK)
 
@@ -38,6 +42,7 @@ __all__ = [
     "ref_decode_paged",
     "ref_decode_sparse",
     "ref_attend_rows",
+    "ref_sparse_prefill",
     "ref_schedule",
     "ref_num_parts",
     "unpack_schedule",
