@@ -261,6 +261,60 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     return res
 
 
+def prefill_work(case) -> dict:
+    """Sparse prefill: FLOP over (query token, head, valid index); bytes = the
+    KV rows once (they are shared by the queries) + q, out, lse, max_logits,
+    indices."""
+    idx = case["indices"]
+    valid = ((idx >= 0) & (idx < case["s_kv"])).sum().item()
+    s_q, h_q, d_qk, d_v = case["s_q"], case["h_q"], case["d_qk"], case["d_v"]
+    flop = valid * h_q * 2 * (d_qk + d_v)
+    byts = case["s_kv"] * d_qk * 2 + s_q * h_q * (d_qk * 2 + d_v * 2 + 8) + idx.numel() * 4
+    return dict(flop=flop, bytes=byts, kv_bytes=case["s_kv"] * d_qk * 2, keys=valid)
+
+
+def bench_prefill(steps: int, warmup: int) -> dict:
+    """The sparse prefill chunk: one mla_sparse_prefill call per step."""
+    import torch
+
+    import mla_paged_kv_amd as mla
+    from synth.configs import make_config
+    import numpy as np
+
+    case = make_config("p")
+    work = prefill_work(case)
+    dev = torch.device("cuda", 0)
+    q, kv, idx = case["q"].to(dev), case["kv"].to(dev), case["indices"].to(dev)
+    meta = mla.mla_get_metadata(np.zeros(case["s_q"], np.int32), 1, case["h_q"], topk=case["topk"],
+                                device=dev)
+    out = torch.empty((case["s_q"], case["h_q"], case["d_v"]), dtype=torch.bfloat16, device=dev)
+    mx = torch.empty((case["s_q"], case["h_q"]), dtype=torch.float32, device=dev)
+    lse = torch.empty_like(mx)
+    ws = torch.empty(max(meta.workspace_bytes(case["d_v"]), 256), dtype=torch.uint8, device=dev)
+
+    def run():
+        mla.mla_sparse_prefill(q, kv, idx, case["softmax_scale"], dv=case["d_v"], meta=meta,
+                               workspace=ws, out=out, max_logits=mx, lse=lse)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = work["flop"] / (ms * 1e-3) / 1e12
+    return dict(workload=case["name"], ms_per_step=round(ms, 5), tflops=round(tflops, 2),
+                roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS,
+                              unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None),
+                schedule=dict(num_parts=meta.num_parts, row_blocks=meta.row_blocks,
+                              max_splits=meta.max_splits, split_units=meta.num_split_units),
+                note="split-KV and combine of one call, timed together")
+
+
 def traffic_path(k) -> str:
     return os.path.join(ROOT, "profiles", f"splitkv_traffic_workload{k}.json")
 
@@ -320,7 +374,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="seeded workload (2 = varlen decode, h_q=128: the headline)")
-    ap.add_argument("--others", default="3,4,5,4f,5f",
+    ap.add_argument("--others", default="3,4,5,4f,5f,p",
                     help="extra workloads timed into 'other_workloads' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -383,6 +437,10 @@ def main():
     others = {}
     for k in [x.strip() for x in args.others.split(",") if x.strip()]:
         if k == str(args.workload):
+            continue
+        if k == "p":
+            others["p"] = bench_prefill(max(10, args.steps // 5), 3)
+            torch.cuda.empty_cache()
             continue
         o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2))
         o["roofline"]["traffic"] = load_traffic(k)

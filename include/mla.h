@@ -173,8 +173,9 @@ int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int32_t batch, int
                             size_t meta_capacity_ints, mla_sched_info* info, void* stream);
 
 /* Workspace bytes a decode call with this metadata needs (0 if nothing is
- * split): fp32 partial outputs [total_slots, rows, d_v] then, 256-byte
- * aligned, fp32 partial log-sum-exps [total_slots, rows]. */
+ * split): fp32 partial outputs [total_slots, rows, d_v] then, each 256-byte
+ * aligned, fp32 partial log-sum-exps [total_slots, rows] and fp32 partial row
+ * maxima [total_slots, rows] (used by mla_sparse_prefill). */
 size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v);
 
 /*
@@ -192,7 +193,7 @@ size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v);
  *   dv             value width (first dv columns of each cache row).
  *   causal         0/1; bottom-right aligned (query i sees positions
  *                  <= L - s_q + i).
- *   softmax_scale  multiplies q.k (commonly d_qk^-0.5).
+ *   softmax_scale  multiplies q.k (commonly d_qk^-0.5); must be > 0.
  *   meta_dev, info metadata (device copy) and header from mla_get_metadata
  *                  in dense mode with the same batch, s_q, h_q.
  *   workspace      device, >= mla_workspace_bytes(info, dv) bytes (may be
@@ -266,6 +267,35 @@ int mla_splitkv_sparse(const void* q, const void* kvcache, const int32_t* indice
 int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,
                 int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
                 size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * mla_sparse_prefill -- sparse MLA prefill (the pages' flash_mla_sparse_fwd:
+ * upstream FlashMLA README, "Sparse MLA Prefill").  For query token i and
+ * head h, over the valid entries t of indices[i] (0 <= t < s_kv; -1 or
+ * >= s_kv is invalid and skipped):
+ *     P_t        = sm_scale * log2(e) * <q[i,h,:], kv[t,:]>
+ *     max_logits = max_t P_t                       (-inf if no valid entry)
+ *     lse        = log2 sum_t 2^P_t                (base 2; -inf if none)
+ *     out        = sum_t 2^(P_t - lse) * kv[t, 0:dv]   (0 if none)
+ *
+ *   q           [s_q, h_q, d_qk] bf16, device.
+ *   kv          [s_kv, h_kv, d_qk] bf16, device (h_kv must be 1).
+ *   indices     [s_q, h_kv, topk] int32, device.
+ *   sm_scale    > 0.
+ *   meta_dev, info  from mla_get_metadata in sparse mode with batch = s_q,
+ *               s_q = 1, the same h_q, h_kv and topk (each query token is a
+ *               unit); its active head count decides which heads are
+ *               computed (the first ones).
+ *   workspace   >= mla_workspace_bytes(info, dv) bytes.
+ *   out         [s_q, h_q, dv] bf16; max_logits [s_q, h_q] fp32 (may be NULL:
+ *               not written); lse [s_q, h_q] fp32, base 2.  Device.
+ * d_qk in {576, 512}, dv = 512.  Errors as for mla_decode_sparse.
+ */
+int mla_sparse_prefill(const void* q, const void* kv, const int32_t* indices, int32_t s_q,
+                       int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
+                       int32_t topk, float sm_scale, const int32_t* meta_dev,
+                       const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                       void* out, float* max_logits, float* lse, void* stream);
 
 /*
  * FP8 KV cache ("FP8 with scale": upstream FlashMLA README, "FP8 KV Cache";

@@ -13,13 +13,16 @@ Entry points mirror the C ABI names:
 * ``mla_get_metadata_device`` -- the same scheduler as a GPU kernel (no sync)
 * ``mla_decode_paged``   -- dense paged decode, once per layer
 * ``mla_decode_sparse``  -- top-k sparse decode, once per layer
+* ``mla_sparse_prefill`` -- top-k sparse prefill (out, max_logits, base-2 lse)
 
 and, for callers of the pages' Python API, ``get_mla_metadata`` /
-``flash_mla_with_kvcache`` wrappers with the pages' argument order.
+``flash_mla_with_kvcache`` / ``flash_mla_sparse_fwd`` wrappers with the
+pages' argument order.
 """
 from ._binding import (  # noqa: F401
     MLAError,
     Metadata,
+    flash_mla_sparse_fwd,
     flash_mla_with_kvcache,
     get_mla_metadata,
     lib_path,
@@ -28,12 +31,14 @@ from ._binding import (  # noqa: F401
     mla_decode_sparse,
     mla_get_metadata,
     mla_get_metadata_device,
+    mla_sparse_prefill,
     mla_workspace_bytes,
 )
 
 __all__ = [
     "MLAError",
     "Metadata",
+    "flash_mla_sparse_fwd",
     "flash_mla_with_kvcache",
     "get_mla_metadata",
     "lib_path",
@@ -42,5 +47,6 @@ __all__ = [
     "mla_decode_sparse",
     "mla_get_metadata",
     "mla_get_metadata_device",
+    "mla_sparse_prefill",
     "mla_workspace_bytes",
 ]

@@ -83,6 +83,9 @@ def _load():
     for name in ("mla_decode_sparse_fp8", "mla_splitkv_sparse_fp8"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = lib.mla_decode_sparse.argtypes
+    lib.mla_sparse_prefill.restype = ctypes.c_int
+    lib.mla_sparse_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, vp, pinfo, vp, sz, vp, vp, vp, vp]
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [vp, pinfo, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
     _lib = lib
@@ -373,6 +376,47 @@ def mla_combine(meta: Metadata, out, lse, workspace, dv: int = 512):
     return out, lse
 
 
+def mla_sparse_prefill(q, kv, indices, sm_scale: float, dv: int = 512, meta: Metadata | None = None,
+                       num_parts: int = 0, workspace=None, out=None, max_logits=None, lse=None):
+    """Sparse MLA prefill: q [s_q, h_q, d_qk], kv [s_kv, 1, d_qk], indices
+    [s_q, 1, topk] -> (out [s_q, h_q, dv] bf16, max_logits [s_q, h_q] fp32,
+    lse [s_q, h_q] fp32 base 2).  ``meta``: sparse-mode metadata with batch =
+    s_q and one query token each (built here when not given)."""
+    lib = _load()
+    _need(q.dim() == 3 and kv.dim() == 3 and indices.dim() == 3, "q [s_q,h_q,d], kv [s_kv,1,d], "
+          "indices [s_q,1,topk]")
+    _need(q.dtype == torch.bfloat16 and kv.dtype == torch.bfloat16, "q and kv must be bf16")
+    _need(indices.dtype == torch.int32, "indices must be int32")
+    _need(q.is_cuda and kv.is_cuda and indices.is_cuda, "all tensors must be on the GPU")
+    _need(q.is_contiguous() and kv.is_contiguous() and indices.is_contiguous(),
+          "tensors must be contiguous")
+    s_q, h_q, d_qk = q.shape
+    s_kv, h_kv, d_kv = kv.shape
+    _need(d_kv == d_qk, "kv row width must equal q's d_qk")
+    _need(indices.shape[:2] == (s_q, h_kv), "indices must be [s_q, h_kv, topk]")
+    topk = indices.shape[2]
+    if meta is None:
+        meta = mla_get_metadata(np.zeros(s_q, np.int32), 1, h_q, h_kv, topk=topk,
+                                num_parts=num_parts, device=q.device)
+    _need(meta.sparse and meta.topk == topk, "metadata must be sparse-mode with the same topk")
+    if out is None:
+        out = torch.empty((s_q, h_q, dv), dtype=torch.bfloat16, device=q.device)
+    if max_logits is None:
+        max_logits = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
+    need = meta.workspace_bytes(dv)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.mla_sparse_prefill(_ptr(q), _ptr(kv), _ptr(indices), s_q, s_kv, h_q, h_kv, d_qk, dv,
+                                topk, float(sm_scale), _ptr(meta.meta_dev), ctypes.byref(meta.info),
+                                _ptr(workspace), ws_bytes, _ptr(out), _ptr(max_logits), _ptr(lse),
+                                _stream(q.device))
+    _check(rc, "mla_sparse_prefill")
+    return out, max_logits, lse
+
+
 # ---- the pages' call shape ------------------------------------------------
 
 def get_mla_metadata(cache_seqlens, num_q_tokens_per_head_k: int, num_heads_k: int,
@@ -414,3 +458,9 @@ def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v: i
                                  softmax_scale=softmax_scale)
     return mla_decode_paged(q, k_cache, block_table, cache_seqlens, head_dim_v,
                             tile_scheduler_metadata, causal=causal, softmax_scale=softmax_scale)
+
+
+def flash_mla_sparse_fwd(q, kv, indices, sm_scale: float, d_v: int = 512):
+    """The pages' ``flash_mla_sparse_fwd(q, kv, indices, sm_scale)``; returns
+    (out, max_logits, lse) with a base-2 lse."""
+    return mla_sparse_prefill(q, kv, indices, sm_scale, dv=d_v)

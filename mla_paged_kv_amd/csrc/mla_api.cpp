@@ -69,27 +69,36 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
 
 enum { kStageSplit = 1, kStageCombine = 2 };
 
+// Workspace: fp32 partial outputs [slots, rows, dv], then (256-byte aligned)
+// partial base-2 LSEs [slots, rows], then partial row maxima [slots, rows].
 void carve_workspace(const mla_sched_info* info, void* workspace, int32_t dv, float** ws_o,
-                     float** ws_lse) {
+                     float** ws_lse, float** ws_max) {
   const size_t o_bytes = size_t(info->total_slots) * info->rows * dv * sizeof(float);
+  const size_t l_bytes = size_t(info->total_slots) * info->rows * sizeof(float);
+  char* w = static_cast<char*>(workspace);
   *ws_o = static_cast<float*>(workspace);
-  *ws_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(o_bytes))
-                      : nullptr;
+  *ws_lse = w ? reinterpret_cast<float*>(w + align256(o_bytes)) : nullptr;
+  *ws_max = w ? reinterpret_cast<float*>(w + align256(o_bytes) + align256(l_bytes)) : nullptr;
 }
 
 int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, int32_t s_q,
                          int32_t h_q, int32_t heads, bool sparse, void* workspace, int32_t dv,
-                         void* out, float* lse, hipStream_t st) {
+                         void* out, float* lse, float* max_logits, bool lse_base2,
+                         hipStream_t st) {
   if (info->num_split_units <= 0) return MLA_OK;
   CombineParams cp;
   float* ws_o;
   float* ws_lse;
-  carve_workspace(info, workspace, dv, &ws_o, &ws_lse);
+  float* ws_max;
+  carve_workspace(info, workspace, dv, &ws_o, &ws_lse, &ws_max);
   cp.meta = meta_dev;
   cp.ws_o = ws_o;
   cp.ws_lse = ws_lse;
+  cp.ws_max = ws_max;
   cp.out = static_cast<uint16_t*>(out);
   cp.lse = lse;
+  cp.max_logits = max_logits;
+  cp.lse_base2 = lse_base2 ? 1 : 0;
   cp.off_num_splits = info->off_num_splits;
   cp.off_split_list = info->off_split_list;
   cp.num_split_units = info->num_split_units;
@@ -113,7 +122,7 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
 int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, bool fp8,
            void* workspace, int32_t dv, void* stream, int stages) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  carve_workspace(info, workspace, dv, &kp.ws_o, &kp.ws_lse);
+  carve_workspace(info, workspace, dv, &kp.ws_o, &kp.ws_lse, &kp.ws_max);
   kp.num_parts = info->num_parts;
   kp.row_blocks = info->row_blocks;
   kp.rows = info->rows;
@@ -123,7 +132,7 @@ int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool spa
   }
   if (stages & kStageCombine)
     return launch_combine_stage(kp.meta, info, kp.s_q, kp.h_q, kp.heads, sparse, workspace, dv,
-                                kp.out, kp.lse, st);
+                                kp.out, kp.lse, kp.max_logits, kp.lse_base2 != 0, st);
   return MLA_OK;
 }
 
@@ -163,7 +172,7 @@ size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v) {
   if (info == nullptr || info->total_slots <= 0 || info->rows <= 0 || d_v <= 0) return 0;
   const size_t o = size_t(info->total_slots) * info->rows * d_v * sizeof(float);
   const size_t l = size_t(info->total_slots) * info->rows * sizeof(float);
-  return mla::align256(o) + mla::align256(l);
+  return mla::align256(o) + 2 * mla::align256(l);
 }
 
 }  // extern "C"
@@ -184,7 +193,8 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
   if (!block_table || !cache_seqlens) return set_error(MLA_E_INVAL, "decode_paged: null block_table/seqlens");
   if (bt_stride < 1) return set_error(MLA_E_INVAL, "decode_paged: bt_stride=%d", bt_stride);
   if (causal != 0 && causal != 1) return set_error(MLA_E_INVAL, "decode_paged: causal=%d", causal);
-  if (!std::isfinite(softmax_scale)) return set_error(MLA_E_INVAL, "decode_paged: softmax_scale not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return set_error(MLA_E_INVAL, "decode_paged: softmax_scale must be positive and finite");
   if (info->num_units != batch)
     return set_error(MLA_E_INVAL, "decode_paged: metadata built for %d units, batch=%d (dense mode?)",
                      info->num_units, batch);
@@ -226,7 +236,8 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
   if (rc != MLA_OK || batch == 0) return rc;
   if (!indices) return set_error(MLA_E_INVAL, "decode_sparse: null indices");
   if (topk < 1) return set_error(MLA_E_INVAL, "decode_sparse: topk=%d", topk);
-  if (!std::isfinite(softmax_scale)) return set_error(MLA_E_INVAL, "decode_sparse: softmax_scale not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return set_error(MLA_E_INVAL, "decode_sparse: softmax_scale must be positive and finite");
   if (int64_t(info->num_units) != int64_t(batch) * s_q)
     return set_error(MLA_E_INVAL, "decode_sparse: metadata built for %d units, batch*s_q=%lld (sparse mode?)",
                      info->num_units, (long long)batch * s_q);
@@ -254,9 +265,64 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
   return launch(kp, info, d_qk, true, fp8, workspace, dv, stream, stages);
 }
 
+int sparse_prefill_impl(const void* q, const void* kv, const int32_t* indices, int32_t s_q,
+                        int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
+                        int32_t topk, float sm_scale, const int32_t* meta_dev,
+                        const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                        void* out, float* max_logits, float* lse, void* stream) {
+  clear_error();
+  if (s_kv < 1) return set_error(MLA_E_INVAL, "sparse_prefill: s_kv=%d", s_kv);
+  // the shared checks see the KV rows as ceil(s_kv / 64) pages of 64
+  const int64_t pages = (int64_t(s_kv) + kPage - 1) / kPage;
+  int rc = check_common(q, kv, s_q, 1, h_q, h_kv, d_qk, dv, int32_t(pages), kPage, meta_dev, info,
+                        workspace, workspace_bytes, out, lse, false);
+  if (rc != MLA_OK || s_q == 0) return rc;
+  if (!indices) return set_error(MLA_E_INVAL, "sparse_prefill: null indices");
+  if (topk < 1) return set_error(MLA_E_INVAL, "sparse_prefill: topk=%d", topk);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return set_error(MLA_E_INVAL, "sparse_prefill: sm_scale must be positive and finite");
+  if (max_logits && !aligned(max_logits, 4))
+    return set_error(MLA_E_INVAL, "sparse_prefill: max_logits needs 4-byte alignment");
+  if (info->num_units != s_q)
+    return set_error(MLA_E_INVAL,
+                     "sparse_prefill: metadata built for %d units, s_q=%d (build it in sparse mode "
+                     "with batch = s_q and one query token each)",
+                     info->num_units, s_q);
+  const int32_t heads = info->rows;
+  if (heads < 1 || heads > h_q)
+    return set_error(MLA_E_INVAL, "sparse_prefill: metadata heads %d outside [1, h_q=%d]", heads, h_q);
+
+  SplitKVParams kp{};
+  kp.q = static_cast<const uint16_t*>(q);
+  kp.kv = static_cast<const uint16_t*>(kv);
+  kp.indices = indices;
+  kp.meta = meta_dev;
+  kp.out = static_cast<uint16_t*>(out);
+  kp.lse = lse;
+  kp.max_logits = max_logits;
+  kp.lse_base2 = 1;
+  kp.s_q = 1;  // every query token is a unit of its own
+  kp.h_q = h_q;
+  kp.heads = heads;
+  kp.num_rows = s_kv;  // an index is valid iff 0 <= idx < s_kv
+  kp.topk = topk;
+  kp.scale_log2 = sm_scale * 1.4426950408889634f;
+  return launch(kp, info, d_qk, true, false, workspace, dv, stream, kStageSplit | kStageCombine);
+}
+
 }  // namespace mla
 
 extern "C" {
+
+int mla_sparse_prefill(const void* q, const void* kv, const int32_t* indices, int32_t s_q,
+                       int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
+                       int32_t topk, float sm_scale, const int32_t* meta_dev,
+                       const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                       void* out, float* max_logits, float* lse, void* stream) {
+  return mla::sparse_prefill_impl(q, kv, indices, s_q, s_kv, h_q, h_kv, d_qk, dv, topk, sm_scale,
+                                  meta_dev, info, workspace, workspace_bytes, out, max_logits, lse,
+                                  stream);
+}
 
 #define MLA_PAGED_ARGS                                                                          \
   const void *q, const void *kvcache, const int32_t *block_table, const int32_t *cache_seqlens, \
@@ -341,7 +407,7 @@ int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t bat
   if (workspace_bytes < mla_workspace_bytes(info, dv))
     return set_error(MLA_E_NOSPC, "combine: workspace too small");
   return launch_combine_stage(meta_dev, info, s_q, h_q, heads, sparse != 0,
-                              const_cast<void*>(workspace), dv, out, lse,
+                              const_cast<void*>(workspace), dv, out, lse, nullptr, false,
                               static_cast<hipStream_t>(stream));
 }
 

@@ -138,6 +138,14 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
     m = mt;
     l = lt;
   }
+  // row maximum of the scaled logits over the splits (when asked for); only
+  // the wavefront that writes the row reaches this point
+  float mx = -__builtin_inff();
+  if (p.max_logits) {
+    for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, p.ws_max[size_t(slot0 + s) * p.rows + row]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  }
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
   const float lse2 = empty ? -__builtin_inff() : m + fast_log2(l);
@@ -161,7 +169,10 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
   w4[2] = uint32_t(f2bf(a1[0])) | (uint32_t(f2bf(a1[1])) << 16);
   w4[3] = uint32_t(f2bf(a1[2])) | (uint32_t(f2bf(a1[3])) << 16);
   *reinterpret_cast<u32x4*>(p.out + qrow * kDV + 8 * lane) = u32x4{w4[0], w4[1], w4[2], w4[3]};
-  if (lane == 0) p.lse[qrow] = lse2 * kLn2;
+  if (lane == 0) {
+    p.lse[qrow] = p.lse_base2 ? lse2 : lse2 * kLn2;
+    if (p.max_logits) p.max_logits[qrow] = mx;
+  }
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {

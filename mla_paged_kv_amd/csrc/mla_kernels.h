@@ -23,6 +23,10 @@ struct SplitKVParams {
   float* lse;                  // [batch, s_q, h_q] fp32 (natural log)
   float* ws_o;                 // [slots, rows, 512] fp32 partial outputs
   float* ws_lse;               // [slots, rows] fp32 partial LSE (base 2)
+  float* max_logits;           // optional [batch, s_q, h_q] fp32 row maxima of the scaled
+                               // logits (base 2); null = not written
+  float* ws_max;               // [slots, rows] fp32 partial maxima (with max_logits)
+  int32_t lse_base2;           // 1: lse is written in base 2, 0: natural log
   int32_t s_q, h_q;
   int32_t heads;      // active heads (first `heads` of h_q)
   int32_t rows;       // query rows per unit
@@ -38,8 +42,11 @@ struct CombineParams {
   const int32_t* meta;
   const float* ws_o;
   const float* ws_lse;
+  const float* ws_max;  // partial maxima (read when max_logits is set)
   uint16_t* out;
   float* lse;
+  float* max_logits;    // optional row maxima output
+  int32_t lse_base2;
   int32_t off_num_splits, off_split_list, num_split_units;
   int32_t max_splits;  // most splits of any unit (picks the combine layout)
   int32_t rows, s_q, h_q, heads;

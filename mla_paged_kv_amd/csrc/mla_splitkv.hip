@@ -332,7 +332,12 @@ void mla_splitkv(SplitKVParams p) {
     if constexpr (SPARSE) {
       const bool ok = m.idx >= 0 && m.idx < p.num_rows;
       g.vmask = __ballot(ok);
-      const int sub = g.vmask ? __shfl(m.idx, __builtin_ctzll(g.vmask)) : 0;
+      // a tile without any valid index: through one buffer resource (pools
+      // below 4 GiB) every lane reads row num_rows, past the end of the
+      // resource, which returns zeros -- the tile is then computed like any
+      // other, fully masked, and adds exactly nothing; with 64-bit addressing
+      // the tile is skipped instead
+      const int sub = g.vmask ? __shfl(m.idx, __builtin_ctzll(g.vmask)) : (WIDE ? 0 : p.num_rows);
       g.idx = ok ? m.idx : sub;
     } else {
       const int vt = m.len - blk * kPage;
@@ -477,6 +482,7 @@ void mla_splitkv(SplitKVParams p) {
   bf16x8 qf[KK];
   f32x16 acc[NCT];
   float m_run = -__builtin_inff();
+  float m_exact = -__builtin_inff();  // exact row maximum of the scaled logits (base 2)
   float l_part = 0.f;
   size_t qrow = 0;
   int n_vis = 0;
@@ -494,6 +500,7 @@ void mla_splitkv(SplitKVParams p) {
   auto reset_state = [&]() __attribute__((always_inline)) {
     seg_first = true;
     m_run = -__builtin_inff();
+    m_exact = -__builtin_inff();
     l_part = 0.f;
   };
 
@@ -524,7 +531,10 @@ void mla_splitkv(SplitKVParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (lse_lane) p.lse[orow] = lse2 * kLn2;
+      if (lse_lane) {
+        p.lse[orow] = p.lse_base2 ? lse2 : lse2 * kLn2;
+        if (p.max_logits) p.max_logits[orow] = m_exact;
+      }
     } else {
       const size_t wrow = size_t(slot) * p.rows + row;
       float* o = p.ws_o + wrow * kDV;
@@ -539,7 +549,10 @@ void mla_splitkv(SplitKVParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (lse_lane) p.ws_lse[wrow] = lse2;
+      if (lse_lane) {
+        p.ws_lse[wrow] = lse2;
+        if (p.max_logits) p.ws_max[wrow] = m_exact;
+      }
     }
   };
 
@@ -624,12 +637,17 @@ void mla_splitkv(SplitKVParams p) {
 #pragma unroll
       for (int v = 0; v < 16; v += 2) mloc = fmaxf(mloc, fmaxf(st[0][v], st[0][v + 1]));
     } else {
+      // sparse: the lane's tokens are 32 half + 4 lgrp + c, c = tok(v, 0) <= 27,
+      // so one shift of the tile mask leaves a 32-bit word tested at
+      // compile-time bit positions
+      uint32_t vm = 0;
+      if constexpr (SPARSE) vm = uint32_t(vmask >> (32 * half + 4 * lgrp));
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = 32 * half + tok(v, lgrp);
         bool vis;
         if constexpr (SPARSE) {
-          vis = (vmask >> t) & 1;
+          vis = (vm >> tok(v, 0)) & 1;
         } else {
           vis = blk * kPage + t < n_vis;
         }
@@ -642,6 +660,7 @@ void mla_splitkv(SplitKVParams p) {
     if (lane < 32) x_max[32 * wave + xl] = mloc;  // maximum over both token halves
     lds_barrier();
     mloc = fmaxf(mloc, x_max[32 * (wave ^ 1) + (xl & 31)]) * p.scale_log2;
+    m_exact = fmaxf(m_exact, mloc);
     const bool grow = mloc > m_run + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? mloc : m_run;
@@ -758,7 +777,7 @@ void mla_splitkv(SplitKVParams p) {
     reset_state();
     const Gather g0 = plan_gather(ct.blk, m0);
     cmask = g0.vmask;
-    if (!SPARSE || cmask != 0) {
+    if (!SPARSE || !WIDE || cmask != 0) {
       if constexpr (FP8)
         gather_fp8(g0, stg_a);
       else
@@ -799,15 +818,15 @@ void mla_splitkv(SplitKVParams p) {
     asm volatile("" : "+v"(nx_ln));
     const int next_q_unit = (ct.last && has_next) ? nt.u : -1;
     if constexpr (FP8) {
-      if (has_next && (!SPARSE || nmask != 0)) gather_fp8(nx_plan, nxt_buf);
-      if (!SPARSE || cmask != 0) {
+      if (has_next && (!SPARSE || !WIDE || nmask != 0)) gather_fp8(nx_plan, nxt_buf);
+      if (!SPARSE || !WIDE || cmask != 0) {
         dequant(cur_buf, buf_a);
         lds_barrier();
         compute_tile(buf_a, ct.blk, cmask, next_q_unit, cur_buf);
       } else if (next_q_unit >= 0) {
         load_q(next_q_unit);
       }
-    } else if (!SPARSE || cmask != 0) {
+    } else if (!SPARSE || !WIDE || cmask != 0) {
       compute_tile(cur_buf, ct.blk, cmask, next_q_unit, x_own);
     } else {
       if (next_q_unit >= 0) load_q(next_q_unit);
@@ -859,7 +878,9 @@ hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, bool fp
   const dim3 grid(groups), block(256);
   // sparse rows are addressed with 32-bit byte offsets while the pool fits
   const uint64_t row_bytes = fp8 ? kFp8RowBytes : uint64_t(d_qk) * 2;
-  const bool wide = uint64_t(p.num_rows) * row_bytes > 0xFFFFFFFFull;
+  // (num_rows + 1 rows keep the past-the-end offset of an all-invalid tile
+  // inside 32 bits)
+  const bool wide = (uint64_t(p.num_rows) + 2) * row_bytes > 0xFFFFFFFFull;
 #define MLA_LAUNCH(D, F)                                                                     \
   do {                                                                                       \
     if (!sparse)                                                                             \

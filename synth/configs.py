@@ -159,6 +159,37 @@ def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
     )
 
 
+def make_prefill_case(seed: int, *, s_q: int, s_kv: int, h_q: int, topk: int, d_qk: int = 576,
+                      d_v: int = 512, invalid_tail: int = 0, past_end: int = 0,
+                      name: str = "sparse prefill") -> dict:
+    """A sparse-prefill case: q [s_q, h_q, d_qk], kv [s_kv, 1, d_qk] bf16
+    normals; query i draws ``topk`` distinct positions of [0, s_kv), sorted;
+    the last ``invalid_tail`` become -1 and the ``past_end`` before them
+    become s_kv + j (also invalid)."""
+    rng = rng_for(seed)
+    q = normal_bf16(rng, (s_q, h_q, d_qk))
+    kv = normal_bf16(rng, (s_kv, 1, d_qk))
+    idx = np.empty((s_q, 1, topk), dtype=np.int32)
+    for i in range(s_q):
+        row = np.sort(rng.choice(s_kv, size=topk, replace=False)).astype(np.int64)
+        if invalid_tail:
+            row[topk - invalid_tail:] = -1
+        if past_end:
+            lo = topk - invalid_tail - past_end
+            row[lo:topk - invalid_tail] = s_kv + np.arange(past_end)
+        idx[i, 0] = row
+    return dict(name=name, prefill=True, q=q, kv=kv, indices=torch.from_numpy(idx), s_q=s_q,
+                s_kv=s_kv, h_q=h_q, topk=topk, d_qk=d_qk, d_v=d_v,
+                softmax_scale=float(d_qk) ** -0.5)
+
+
+# Sparse prefill: one 4096-token chunk over a 32768-token context, every query
+# with its own top-2048 positions (DeepSeek-style sparse attention shapes: 128
+# heads, 576-wide latent rows).
+PREFILL_CONFIG = dict(name="sparse prefill: s_q=4096 s_kv=32768 h_q=128 d_qk=576 d_v=512 topk 2048",
+                      s_q=4096, s_kv=32768, h_q=128, topk=2048)
+
+
 def _c2_lens(rng):
     return rng.integers(1, 4097, size=64)
 
@@ -200,8 +231,10 @@ FP8_CONFIGS = {
 
 
 def make_config(k) -> dict:
-    """The five named workloads (k = 1..5), seed 1000 + k, and their FP8-cache
-    variants ("4f", "5f")."""
+    """The five named workloads (k = 1..5), seed 1000 + k, their FP8-cache
+    variants ("4f", "5f") and the sparse prefill chunk ("p", seed 1100)."""
+    if k == "p":
+        return make_prefill_case(1100, **PREFILL_CONFIG)
     if isinstance(k, str) and k in FP8_CONFIGS:
         spec = dict(FP8_CONFIGS[k])
         seed = 1000 + int(k[:-1])

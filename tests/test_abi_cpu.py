@@ -32,12 +32,13 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = header_functions()
-    for n in ["mla_get_metadata", "mla_get_metadata_device", "mla_decode_paged", "mla_decode_sparse", "mla_workspace_bytes",
+    for n in ["mla_get_metadata", "mla_get_metadata_device", "mla_sparse_prefill",
+              "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_decode_paged", "mla_decode_sparse", "mla_workspace_bytes",
               "mla_strerror", "mla_last_error", "mla_version", "mla_default_num_parts",
               "mla_metadata_capacity"]:
         assert n in names
@@ -254,6 +255,7 @@ def test_workspace_bytes(lib):
     rc, meta, info = _raw_meta(lib, [64, 200], P=512, rows=16)
     n = lib.mla_workspace_bytes(ctypes.byref(info), 512)
     slots, rows = info.total_slots, info.rows
-    assert n == -(-slots * rows * 512 * 4 // 256) * 256 + -(-slots * rows * 4 // 256) * 256
+    # partial outputs, then partial LSEs and partial row maxima, each 256-byte aligned
+    assert n == -(-slots * rows * 512 * 4 // 256) * 256 + 2 * (-(-slots * rows * 4 // 256) * 256)
     rc, meta, info = _raw_meta(lib, [64, 64], P=2, rows=16)
     assert info.total_slots == 0 and lib.mla_workspace_bytes(ctypes.byref(info), 512) == 0

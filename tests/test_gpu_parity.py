@@ -216,3 +216,32 @@ def test_named_workload_full_size(k):
     if k == 3:
         batches = list(range(0, 128, 9))  # 15 of 128 requests (each 2 x 128 rows x 4096 keys)
     _check(case, num_parts=0, batches=batches, what=f"workload {k}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_sparse_whole_tiles_of_invalid_indices(fp8):
+    """Tiles whose 64 indices are all invalid are read as zero rows and fully
+    masked: the result equals the oracle's and does not change when every
+    row the indices do not select (row 0 included) is NaN-poisoned."""
+    d_qk = 576
+    case = make_sparse_case(45, B=3, s_q=1, h_q=16, active_h_q=16, topk=320, cache_len=4096,
+                            invalid_tail=190, d_qk=d_qk, kv_fp8=fp8)
+    idx = case["indices"].clone()
+    idx[1, 0, :] = -1  # a query with no valid index at all
+    case = dict(case, indices=idx)
+    _check(case, num_parts=0, what=f"whole invalid tiles fp8={fp8}")
+    d = to_device(case)
+    meta = metadata(case, num_parts=2)
+    o1, l1 = run_gpu(d, meta)
+    row_w = case["kvcache"].shape[-1]
+    kv = case["kvcache"].clone().view(-1, row_w)
+    keep = torch.zeros(kv.shape[0], dtype=torch.bool)
+    iv = idx.flatten()
+    keep[iv[iv >= 0].long()] = True
+    if fp8:
+        kv[~keep] = 0xFF
+    else:
+        kv[~keep] = float("nan")
+    o2, l2 = run_gpu(dict(d, kvcache=kv.view_as(case["kvcache"]).cuda()), meta)
+    assert torch.equal(o1[:, :, :16], o2[:, :, :16]) and torch.equal(l1[:, :, :16], l2[:, :, :16])
+    assert torch.all(torch.isneginf(l1[1, 0, :16])) and torch.all(o1[1, 0, :16] == 0)
