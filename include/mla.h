@@ -36,8 +36,9 @@
  *    Errors are detected before any work is enqueued; nothing is written on
  *    error.  mla_strerror() names a code, mla_last_error() gives details.
  *  - Supported by the kernels: h_kv == 1, page_block_size == 64, d_qk in
- *    {576, 512}, d_v == 512 (<= d_qk), bf16 q/kvcache/out.  Anything else
- *    returns MLA_E_NOTSUP.
+ *    {576, 512}, d_v == 512 (<= d_qk); q/kvcache/out bf16, or fp16 through the
+ *    *_f16 entry points, or a bf16 q with an FP8-with-scale cache through the
+ *    *_fp8 entry points.  Anything else returns MLA_E_NOTSUP.
  */
 #ifndef MLA_PAGED_KV_MLA_H
 #define MLA_PAGED_KV_MLA_H
@@ -296,6 +297,49 @@ int mla_sparse_prefill(const void* q, const void* kv, const int32_t* indices, in
                        int32_t topk, float sm_scale, const int32_t* meta_dev,
                        const mla_sched_info* info, void* workspace, size_t workspace_bytes,
                        void* out, float* max_logits, float* lse, void* stream);
+
+/*
+ * fp16 inputs (the pages list BF16 and FP16: sourcepulse.org FlashMLA
+ * summary, "How It Works" and "Highlighted Details").  Same arguments,
+ * checks, metadata and workspace as the entry point without the suffix, with
+ * q, kvcache (kv) and out in IEEE fp16 instead of bf16: the products run on
+ * the fp16 matrix cores, P is rounded to fp16 before the PV product and the
+ * output to fp16 (nearest even); lse (and max_logits) stay fp32.
+ */
+int mla_decode_paged_f16(const void* q, const void* kvcache, const int32_t* block_table,
+                         const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                         int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                         int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                         float softmax_scale, const int32_t* meta_dev,
+                         const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                         void* out, float* lse, void* stream);
+int mla_splitkv_paged_f16(const void* q, const void* kvcache, const int32_t* block_table,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                          int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                          int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                          float softmax_scale, const int32_t* meta_dev,
+                          const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, void* stream);
+int mla_decode_sparse_f16(const void* q, const void* kvcache, const int32_t* indices,
+                          int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                          int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                          float softmax_scale, const int32_t* meta_dev,
+                          const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, void* stream);
+int mla_splitkv_sparse_f16(const void* q, const void* kvcache, const int32_t* indices,
+                           int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                           int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
+                           float softmax_scale, const int32_t* meta_dev,
+                           const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                           void* out, float* lse, void* stream);
+int mla_combine_f16(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch,
+                    int32_t s_q, int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
+                    size_t workspace_bytes, void* out, float* lse, void* stream);
+int mla_sparse_prefill_f16(const void* q, const void* kv, const int32_t* indices, int32_t s_q,
+                           int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
+                           int32_t topk, float sm_scale, const int32_t* meta_dev,
+                           const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                           void* out, float* max_logits, float* lse, void* stream);
 
 /*
  * FP8 KV cache ("FP8 with scale": upstream FlashMLA README, "FP8 KV Cache";

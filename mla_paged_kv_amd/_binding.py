@@ -83,11 +83,20 @@ def _load():
     for name in ("mla_decode_sparse_fp8", "mla_splitkv_sparse_fp8"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = lib.mla_decode_sparse.argtypes
-    lib.mla_sparse_prefill.restype = ctypes.c_int
-    lib.mla_sparse_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+    for name in ("mla_decode_paged_f16", "mla_splitkv_paged_f16"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = lib.mla_decode_paged.argtypes
+    for name in ("mla_decode_sparse_f16", "mla_splitkv_sparse_f16"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = lib.mla_decode_sparse.argtypes
+    for name in ("mla_sparse_prefill", "mla_sparse_prefill_f16"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.c_float, vp, pinfo, vp, sz, vp, vp, vp, vp]
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [vp, pinfo, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
+    lib.mla_combine_f16.restype = ctypes.c_int
+    lib.mla_combine_f16.argtypes = lib.mla_combine.argtypes
     _lib = lib
     return lib
 
@@ -252,11 +261,11 @@ def _need(cond, msg):
 def _prep_outputs(q, meta, dv, workspace, out, lse):
     B, s_q, h_q, _ = q.shape
     if out is None:
-        out = torch.empty((B, s_q, h_q, dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, s_q, h_q, dv), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
-    _need(out.shape == (B, s_q, h_q, dv) and out.dtype == torch.bfloat16 and out.is_contiguous(),
-          "out must be contiguous bf16 [B, s_q, h_q, dv]")
+    _need(out.shape == (B, s_q, h_q, dv) and out.dtype == q.dtype and out.is_contiguous(),
+          "out must be contiguous [B, s_q, h_q, dv] of q's dtype")
     _need(lse.shape == (B, s_q, h_q) and lse.dtype == torch.float32 and lse.is_contiguous(),
           "lse must be contiguous fp32 [B, s_q, h_q]")
     need = meta.workspace_bytes(dv)
@@ -269,16 +278,21 @@ def _prep_outputs(q, meta, dv, workspace, out, lse):
 FP8_ROW_BYTES = 656  # "FP8 with scale" cache row: 512 e4m3, 4 fp32 scales, 64 bf16
 
 
+_ELEM = {torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
 def _kv_format(q, kvcache):
-    """'bf16' or 'fp8' (uint8 rows of 656 bytes, d_qk must be 576)."""
+    """'bf16', 'f16' (q, cache and out fp16) or 'fp8' (bf16 q, uint8 cache rows
+    of 656 bytes, d_qk must be 576)."""
     if kvcache.dtype == torch.uint8:
+        _need(q.dtype == torch.bfloat16, "an FP8 cache takes a bf16 q")
         _need(kvcache.shape[-1] == FP8_ROW_BYTES, "an FP8 cache has 656-byte rows")
         _need(q.shape[-1] == 576, "the FP8 cache format needs d_qk = 576")
         return "fp8"
-    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16,
-          "q and kvcache must be bf16 (or kvcache uint8 FP8-with-scale rows)")
+    _need(q.dtype in _ELEM and kvcache.dtype == q.dtype,
+          "q and kvcache must both be bf16 or both fp16 (or kvcache uint8 FP8-with-scale rows)")
     _need(kvcache.shape[-1] == q.shape[-1], "kvcache row width must equal q's d_qk")
-    return "bf16"
+    return _ELEM[q.dtype]
 
 
 def _stream(device):
@@ -294,12 +308,9 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
     :func:`mla_combine` with the same workspace, out and lse)."""
     lib = _load()
     _need(q.dim() == 4 and kvcache.dim() == 4, "q is [B, s_q, h_q, d_qk], kvcache [blocks, 64, h_kv, d_qk]")
-    _need(q.dtype == torch.bfloat16, "q must be bf16")
-    fp8 = _kv_format(q, kvcache) == "fp8"
-    if fp8:
-        fn = lib.mla_decode_paged_fp8 if stage == "all" else lib.mla_splitkv_paged_fp8
-    else:
-        fn = lib.mla_decode_paged if stage == "all" else lib.mla_splitkv_paged
+    fmt = _kv_format(q, kvcache)
+    sfx = {"bf16": "", "f16": "_f16", "fp8": "_fp8"}[fmt]
+    fn = getattr(lib, ("mla_decode_paged" if stage == "all" else "mla_splitkv_paged") + sfx)
     _need(q.is_cuda and kvcache.is_cuda and block_table.is_cuda and cache_seqlens.is_cuda,
           "all tensors must be on the GPU")
     _need(q.is_contiguous() and kvcache.is_contiguous() and block_table.is_contiguous()
@@ -335,12 +346,9 @@ def mla_decode_sparse(q, kvcache, indices, dv: int, meta: Metadata,
     """Top-k sparse decode; heads past the metadata's active count are not written."""
     lib = _load()
     _need(q.dim() == 4 and kvcache.dim() == 4 and indices.dim() == 3, "bad ranks")
-    _need(q.dtype == torch.bfloat16, "q must be bf16")
-    fp8 = _kv_format(q, kvcache) == "fp8"
-    if fp8:
-        fn = lib.mla_decode_sparse_fp8 if stage == "all" else lib.mla_splitkv_sparse_fp8
-    else:
-        fn = lib.mla_decode_sparse if stage == "all" else lib.mla_splitkv_sparse
+    fmt = _kv_format(q, kvcache)
+    sfx = {"bf16": "", "f16": "_f16", "fp8": "_fp8"}[fmt]
+    fn = getattr(lib, ("mla_decode_sparse" if stage == "all" else "mla_splitkv_sparse") + sfx)
     _need(indices.dtype == torch.int32, "indices must be int32")
     _need(q.is_cuda and kvcache.is_cuda and indices.is_cuda, "all tensors must be on the GPU")
     _need(q.is_contiguous() and kvcache.is_contiguous() and indices.is_contiguous(),
@@ -369,7 +377,9 @@ def mla_combine(meta: Metadata, out, lse, workspace, dv: int = 512):
     lib = _load()
     B, s_q, h_q, _ = out.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.mla_combine(_ptr(meta.meta_dev), ctypes.byref(meta.info), B, s_q, h_q, dv,
+    _need(out.dtype in _ELEM, "out must be bf16 or fp16")
+    fn = lib.mla_combine_f16 if out.dtype == torch.float16 else lib.mla_combine
+    rc = fn(_ptr(meta.meta_dev), ctypes.byref(meta.info), B, s_q, h_q, dv,
                          1 if meta.sparse else 0, _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
                          _stream(out.device))
     _check(rc, "mla_combine")
@@ -385,7 +395,7 @@ def mla_sparse_prefill(q, kv, indices, sm_scale: float, dv: int = 512, meta: Met
     lib = _load()
     _need(q.dim() == 3 and kv.dim() == 3 and indices.dim() == 3, "q [s_q,h_q,d], kv [s_kv,1,d], "
           "indices [s_q,1,topk]")
-    _need(q.dtype == torch.bfloat16 and kv.dtype == torch.bfloat16, "q and kv must be bf16")
+    _need(q.dtype in _ELEM and kv.dtype == q.dtype, "q and kv must both be bf16 or both fp16")
     _need(indices.dtype == torch.int32, "indices must be int32")
     _need(q.is_cuda and kv.is_cuda and indices.is_cuda, "all tensors must be on the GPU")
     _need(q.is_contiguous() and kv.is_contiguous() and indices.is_contiguous(),
@@ -400,7 +410,7 @@ def mla_sparse_prefill(q, kv, indices, sm_scale: float, dv: int = 512, meta: Met
                                 num_parts=num_parts, device=q.device)
     _need(meta.sparse and meta.topk == topk, "metadata must be sparse-mode with the same topk")
     if out is None:
-        out = torch.empty((s_q, h_q, dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((s_q, h_q, dv), dtype=q.dtype, device=q.device)
     if max_logits is None:
         max_logits = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -409,7 +419,8 @@ def mla_sparse_prefill(q, kv, indices, sm_scale: float, dv: int = 512, meta: Met
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.mla_sparse_prefill(_ptr(q), _ptr(kv), _ptr(indices), s_q, s_kv, h_q, h_kv, d_qk, dv,
+    fn = lib.mla_sparse_prefill_f16 if q.dtype == torch.float16 else lib.mla_sparse_prefill
+    rc = fn(_ptr(q), _ptr(kv), _ptr(indices), s_q, s_kv, h_q, h_kv, d_qk, dv,
                                 topk, float(sm_scale), _ptr(meta.meta_dev), ctypes.byref(meta.info),
                                 _ptr(workspace), ws_bytes, _ptr(out), _ptr(max_logits), _ptr(lse),
                                 _stream(q.device))
@@ -452,7 +463,7 @@ def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v: i
             k_cache = k_cache.view(torch.uint8)
         _need(k_cache.shape[-1] == FP8_ROW_BYTES, "is_fp8_kvcache: rows must be 656 bytes")
     else:
-        _need(k_cache.dtype == torch.bfloat16, "the cache must be bf16 unless is_fp8_kvcache")
+        _need(k_cache.dtype in _ELEM, "the cache must be bf16 or fp16 unless is_fp8_kvcache")
     if indices is not None:
         return mla_decode_sparse(q, k_cache, indices, head_dim_v, tile_scheduler_metadata,
                                  softmax_scale=softmax_scale)

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
 SOURCES = ["mla_sched.cpp", "mla_sched_dev.hip", "mla_api.cpp", "mla_splitkv.hip",
-           "mla_combine.hip"]
+           "mla_splitkv_f16.hip", "mla_combine.hip"]
 
 # Packed-FP32 VALU ops are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

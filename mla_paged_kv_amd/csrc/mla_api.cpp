@@ -83,7 +83,7 @@ void carve_workspace(const mla_sched_info* info, void* workspace, int32_t dv, fl
 
 int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, int32_t s_q,
                          int32_t h_q, int32_t heads, bool sparse, void* workspace, int32_t dv,
-                         void* out, float* lse, float* max_logits, bool lse_base2,
+                         void* out, float* lse, float* max_logits, bool lse_base2, bool f16,
                          hipStream_t st) {
   if (info->num_split_units <= 0) return MLA_OK;
   CombineParams cp;
@@ -99,6 +99,7 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
   cp.lse = lse;
   cp.max_logits = max_logits;
   cp.lse_base2 = lse_base2 ? 1 : 0;
+  cp.out_f16 = f16 ? 1 : 0;
   cp.off_num_splits = info->off_num_splits;
   cp.off_split_list = info->off_split_list;
   cp.num_split_units = info->num_split_units;
@@ -120,19 +121,19 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
 }
 
 int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool sparse, bool fp8,
-           void* workspace, int32_t dv, void* stream, int stages) {
+           bool f16, void* workspace, int32_t dv, void* stream, int stages) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   carve_workspace(info, workspace, dv, &kp.ws_o, &kp.ws_lse, &kp.ws_max);
   kp.num_parts = info->num_parts;
   kp.row_blocks = info->row_blocks;
   kp.rows = info->rows;
   if (stages & kStageSplit) {
-    const hipError_t e = launch_splitkv(kp, d_qk, sparse, fp8, st);
+    const hipError_t e = launch_splitkv(kp, d_qk, sparse, fp8, f16, st);
     if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
   if (stages & kStageCombine)
     return launch_combine_stage(kp.meta, info, kp.s_q, kp.h_q, kp.heads, sparse, workspace, dv,
-                                kp.out, kp.lse, kp.max_logits, kp.lse_base2 != 0, st);
+                                kp.out, kp.lse, kp.max_logits, kp.lse_base2 != 0, f16, st);
   return MLA_OK;
 }
 
@@ -185,7 +186,7 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
                       int32_t page_block_size, int32_t bt_stride, int32_t causal,
                       float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
                       void* workspace, size_t workspace_bytes, void* out, float* lse,
-                      void* stream, int stages, bool fp8) {
+                      void* stream, int stages, bool fp8, bool f16) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
                         meta_dev, info, workspace, workspace_bytes, out, lse, fp8);
@@ -221,7 +222,7 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
   kp.topk = 0;
   kp.causal = causal;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, false, fp8, workspace, dv, stream, stages);
+  return launch(kp, info, d_qk, false, fp8, f16, workspace, dv, stream, stages);
 }
 
 int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indices,
@@ -229,7 +230,7 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
                        int32_t dv, int32_t num_blocks, int32_t page_block_size, int32_t topk,
                        float softmax_scale, const int32_t* meta_dev,
                        const mla_sched_info* info, void* workspace, size_t workspace_bytes,
-                       void* out, float* lse, void* stream, int stages, bool fp8) {
+                       void* out, float* lse, void* stream, int stages, bool fp8, bool f16) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
                         meta_dev, info, workspace, workspace_bytes, out, lse, fp8);
@@ -262,14 +263,14 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
   kp.topk = topk;
   kp.causal = 0;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, true, fp8, workspace, dv, stream, stages);
+  return launch(kp, info, d_qk, true, fp8, f16, workspace, dv, stream, stages);
 }
 
 int sparse_prefill_impl(const void* q, const void* kv, const int32_t* indices, int32_t s_q,
                         int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
                         int32_t topk, float sm_scale, const int32_t* meta_dev,
                         const mla_sched_info* info, void* workspace, size_t workspace_bytes,
-                        void* out, float* max_logits, float* lse, void* stream) {
+                        void* out, float* max_logits, float* lse, void* stream, bool f16) {
   clear_error();
   if (s_kv < 1) return set_error(MLA_E_INVAL, "sparse_prefill: s_kv=%d", s_kv);
   // the shared checks see the KV rows as ceil(s_kv / 64) pages of 64
@@ -307,7 +308,7 @@ int sparse_prefill_impl(const void* q, const void* kv, const int32_t* indices, i
   kp.num_rows = s_kv;  // an index is valid iff 0 <= idx < s_kv
   kp.topk = topk;
   kp.scale_log2 = sm_scale * 1.4426950408889634f;
-  return launch(kp, info, d_qk, true, false, workspace, dv, stream, kStageSplit | kStageCombine);
+  return launch(kp, info, d_qk, true, false, f16, workspace, dv, stream, kStageSplit | kStageCombine);
 }
 
 }  // namespace mla
@@ -321,7 +322,17 @@ int mla_sparse_prefill(const void* q, const void* kv, const int32_t* indices, in
                        void* out, float* max_logits, float* lse, void* stream) {
   return mla::sparse_prefill_impl(q, kv, indices, s_q, s_kv, h_q, h_kv, d_qk, dv, topk, sm_scale,
                                   meta_dev, info, workspace, workspace_bytes, out, max_logits, lse,
-                                  stream);
+                                  stream, false);
+}
+
+int mla_sparse_prefill_f16(const void* q, const void* kv, const int32_t* indices, int32_t s_q,
+                           int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
+                           int32_t topk, float sm_scale, const int32_t* meta_dev,
+                           const mla_sched_info* info, void* workspace, size_t workspace_bytes,
+                           void* out, float* max_logits, float* lse, void* stream) {
+  return mla::sparse_prefill_impl(q, kv, indices, s_q, s_kv, h_q, h_kv, d_qk, dv, topk, sm_scale,
+                                  meta_dev, info, workspace, workspace_bytes, out, max_logits, lse,
+                                  stream, true);
 }
 
 #define MLA_PAGED_ARGS                                                                          \
@@ -345,40 +356,57 @@ int mla_sparse_prefill(const void* q, const void* kv, const int32_t* indices, in
       softmax_scale, meta_dev, info, workspace, workspace_bytes, out, lse, stream
 
 int mla_decode_paged(MLA_PAGED_ARGS) {
-  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, false);
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, false, false);
 }
 
 int mla_splitkv_paged(MLA_PAGED_ARGS) {
-  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, false);
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, false, false);
 }
 
 int mla_decode_sparse(MLA_SPARSE_ARGS) {
-  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, false);
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, false, false);
 }
 
 int mla_splitkv_sparse(MLA_SPARSE_ARGS) {
-  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, false);
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, false, false);
 }
 
 int mla_decode_paged_fp8(MLA_PAGED_ARGS) {
-  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, true);
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, true, false);
 }
 
 int mla_splitkv_paged_fp8(MLA_PAGED_ARGS) {
-  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, true);
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, true, false);
 }
 
 int mla_decode_sparse_fp8(MLA_SPARSE_ARGS) {
-  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, true);
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, true, false);
 }
 
 int mla_splitkv_sparse_fp8(MLA_SPARSE_ARGS) {
-  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, true);
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, true, false);
 }
 
-int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,
-                int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
-                size_t workspace_bytes, void* out, float* lse, void* stream) {
+int mla_decode_paged_f16(MLA_PAGED_ARGS) {
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit | mla::kStageCombine, false, true);
+}
+
+int mla_splitkv_paged_f16(MLA_PAGED_ARGS) {
+  return mla::decode_paged_impl(MLA_PAGED_PASS, mla::kStageSplit, false, true);
+}
+
+int mla_decode_sparse_f16(MLA_SPARSE_ARGS) {
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit | mla::kStageCombine, false, true);
+}
+
+int mla_splitkv_sparse_f16(MLA_SPARSE_ARGS) {
+  return mla::decode_sparse_impl(MLA_SPARSE_PASS, mla::kStageSplit, false, true);
+}
+
+static int combine_impl(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch,
+                        int32_t s_q, int32_t h_q, int32_t dv, int32_t sparse,
+                        const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                        void* stream, int f16) {
   using namespace mla;
   clear_error();
   if (info == nullptr) return set_error(MLA_E_INVAL, "combine: null info");
@@ -407,8 +435,22 @@ int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t bat
   if (workspace_bytes < mla_workspace_bytes(info, dv))
     return set_error(MLA_E_NOSPC, "combine: workspace too small");
   return launch_combine_stage(meta_dev, info, s_q, h_q, heads, sparse != 0,
-                              const_cast<void*>(workspace), dv, out, lse, nullptr, false,
+                              const_cast<void*>(workspace), dv, out, lse, nullptr, false, f16 != 0,
                               static_cast<hipStream_t>(stream));
+}
+
+int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,
+                int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
+                size_t workspace_bytes, void* out, float* lse, void* stream) {
+  return combine_impl(meta_dev, info, batch, s_q, h_q, dv, sparse, workspace, workspace_bytes, out,
+                      lse, stream, 0);
+}
+
+int mla_combine_f16(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch,
+                    int32_t s_q, int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
+                    size_t workspace_bytes, void* out, float* lse, void* stream) {
+  return combine_impl(meta_dev, info, batch, s_q, h_q, dv, sparse, workspace, workspace_bytes, out,
+                      lse, stream, 1);
 }
 
 }  // extern "C"

@@ -164,10 +164,13 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
   }
   const size_t qrow = (size_t(b) * p.s_q + iq) * p.h_q + h;
   uint32_t w4[4];
-  w4[0] = uint32_t(f2bf(a0[0])) | (uint32_t(f2bf(a0[1])) << 16);
-  w4[1] = uint32_t(f2bf(a0[2])) | (uint32_t(f2bf(a0[3])) << 16);
-  w4[2] = uint32_t(f2bf(a1[0])) | (uint32_t(f2bf(a1[1])) << 16);
-  w4[3] = uint32_t(f2bf(a1[2])) | (uint32_t(f2bf(a1[3])) << 16);
+  auto cvt = [&](float x) -> uint32_t {  // to the 16-bit output type, nearest even
+    return p.out_f16 ? uint32_t(__builtin_bit_cast(unsigned short, (_Float16)x)) : uint32_t(f2bf(x));
+  };
+  w4[0] = cvt(a0[0]) | (cvt(a0[1]) << 16);
+  w4[1] = cvt(a0[2]) | (cvt(a0[3]) << 16);
+  w4[2] = cvt(a1[0]) | (cvt(a1[1]) << 16);
+  w4[3] = cvt(a1[2]) | (cvt(a1[3]) << 16);
   *reinterpret_cast<u32x4*>(p.out + qrow * kDV + 8 * lane) = u32x4{w4[0], w4[1], w4[2], w4[3]};
   if (lane == 0) {
     p.lse[qrow] = p.lse_base2 ? lse2 : lse2 * kLn2;

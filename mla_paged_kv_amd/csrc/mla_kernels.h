@@ -13,7 +13,7 @@ constexpr int kMetaHeaderInts = 16;  // int32 header ahead of part_ptr in the me
 constexpr int kFp8RowBytes = 656;
 
 struct SplitKVParams {
-  const uint16_t* q;           // [batch, s_q, h_q, d_qk] bf16
+  const uint16_t* q;           // [batch, s_q, h_q, d_qk] bf16 (fp16 for the fp16 kernels)
   const uint16_t* kv;          // [num_blocks * 64] rows: d_qk bf16, or 656-byte FP8 rows (h_kv = 1)
   const int32_t* block_table;  // dense: [batch, bt_stride]
   const int32_t* seqlens;      // dense: [batch]
@@ -49,12 +49,14 @@ struct CombineParams {
   int32_t lse_base2;
   int32_t off_num_splits, off_split_list, num_split_units;
   int32_t max_splits;  // most splits of any unit (picks the combine layout)
+  int32_t out_f16;     // 1: out is fp16, 0: bf16
   int32_t rows, s_q, h_q, heads;
   int32_t sparse;
 };
 
-hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, bool fp8,
+hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, bool fp8, bool f16,
                           hipStream_t stream);
+hipError_t launch_splitkv_f16(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace mla

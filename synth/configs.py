@@ -7,7 +7,8 @@ Recipe (shared by every config):
 * Draw order: sequence lengths -> block permutation -> q -> kvcache ->
   sparse index positions.
 * Values are float32 standard normals rounded once to bfloat16 (round to
-  nearest even, by torch's cast), drawn in chunks of 2**24 values.
+  nearest even, by torch's cast), drawn in chunks of 2**24 values; fp16
+  cases round the same draws to fp16 instead.
 * Logical block j of request b lives in physical block ``block_table[b][j]``.
   Physical blocks are a random permutation of the pool, handed out in batch
   order; table entries past a request's last block are -1 (except the tiny
@@ -41,12 +42,13 @@ def bf16_from_f32(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
 
 
-def normal_bf16(rng: np.random.Generator, shape) -> torch.Tensor:
+def normal_bf16(rng: np.random.Generator, shape, dtype=torch.bfloat16) -> torch.Tensor:
+    """Float32 standard normals rounded once to ``dtype`` (bf16, or fp16)."""
     n = int(np.prod(shape))
-    out = torch.empty(n, dtype=torch.bfloat16)
+    out = torch.empty(n, dtype=dtype)
     for s in range(0, n, CHUNK):
         e = min(n, s + CHUNK)
-        out[s:e] = bf16_from_f32(rng.standard_normal(e - s, dtype=np.float32))
+        out[s:e] = torch.from_numpy(rng.standard_normal(e - s, dtype=np.float32)).to(dtype)
     return out.view(*shape)
 
 
@@ -86,7 +88,7 @@ def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
                     seqlen_sampler=None, d_qk: int = 576, d_v: int = 512, h_kv: int = 1,
                     causal: bool = False, spare_frac: float = 0.0, table_width=None,
                     reshape_table: bool = False, name: str = "dense", kv_fp8: bool = False,
-                    fp8_spread: float = 0.0) -> dict:
+                    fp8_spread: float = 0.0, dtype=torch.bfloat16) -> dict:
     """A dense paged-decode case.  ``seqlens`` fixed, or drawn by ``seqlen_sampler(rng)``.
     ``kv_fp8``: the cache is FP8 with scale (d_qk must be 576)."""
     assert not kv_fp8 or d_qk == 576
@@ -108,11 +110,11 @@ def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
         width = int(table_width) if table_width is not None else max(1, int(nblocks.max(initial=0)))
         perm = rng.permutation(pool).astype(np.int32)
         table = _table_from_perm(perm, nblocks, width)
-    q = normal_bf16(rng, (B, s_q, h_q, d_qk))
+    q = normal_bf16(rng, (B, s_q, h_q, d_qk), dtype)
     if kv_fp8:
         kv = fp8_rows(rng, pool * PAGE * h_kv, fp8_spread).view(pool, PAGE, h_kv, FP8_ROW)
     else:
-        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
+        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk), dtype)
     return dict(
         name=name, sparse=False, q=q, kvcache=kv, kv_fp8=kv_fp8,
         block_table=torch.from_numpy(table),
@@ -126,7 +128,7 @@ def make_dense_case(seed: int, *, B: int, s_q: int, h_q: int, seqlens=None,
 def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
                      topk: int, cache_len: int, invalid_tail: int, d_qk: int = 512,
                      d_v: int = 512, h_kv: int = 1, name: str = "sparse", kv_fp8: bool = False,
-                     fp8_spread: float = 0.0) -> dict:
+                     fp8_spread: float = 0.0, dtype=torch.bfloat16) -> dict:
     """A top-k sparse-decode case: every request owns ``cache_len`` tokens of a
     shared pool; each query token draws ``topk`` distinct positions, sorted,
     and the last ``invalid_tail`` entries become -1."""
@@ -136,11 +138,11 @@ def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
     perm = rng.permutation(pool).astype(np.int32)
     table = perm.reshape(B, width)
     assert not kv_fp8 or d_qk == 576
-    q = normal_bf16(rng, (B, s_q, h_q, d_qk))
+    q = normal_bf16(rng, (B, s_q, h_q, d_qk), dtype)
     if kv_fp8:
         kv = fp8_rows(rng, pool * PAGE * h_kv, fp8_spread).view(pool, PAGE, h_kv, FP8_ROW)
     else:
-        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
+        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk), dtype)
     idx = np.empty((B, s_q, topk), dtype=np.int32)
     for b in range(B):
         for i in range(s_q):
@@ -161,14 +163,14 @@ def make_sparse_case(seed: int, *, B: int, s_q: int, h_q: int, active_h_q: int,
 
 def make_prefill_case(seed: int, *, s_q: int, s_kv: int, h_q: int, topk: int, d_qk: int = 576,
                       d_v: int = 512, invalid_tail: int = 0, past_end: int = 0,
-                      name: str = "sparse prefill") -> dict:
+                      name: str = "sparse prefill", dtype=torch.bfloat16) -> dict:
     """A sparse-prefill case: q [s_q, h_q, d_qk], kv [s_kv, 1, d_qk] bf16
     normals; query i draws ``topk`` distinct positions of [0, s_kv), sorted;
     the last ``invalid_tail`` become -1 and the ``past_end`` before them
     become s_kv + j (also invalid)."""
     rng = rng_for(seed)
-    q = normal_bf16(rng, (s_q, h_q, d_qk))
-    kv = normal_bf16(rng, (s_kv, 1, d_qk))
+    q = normal_bf16(rng, (s_q, h_q, d_qk), dtype)
+    kv = normal_bf16(rng, (s_kv, 1, d_qk), dtype)
     idx = np.empty((s_q, 1, topk), dtype=np.int32)
     for i in range(s_q):
         row = np.sort(rng.choice(s_kv, size=topk, replace=False)).astype(np.int64)
