@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512) on 1 GPU"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-KERNEL_SOURCES = ["mla_paged_kv_amd/csrc/mla_splitkv.hip", "mla_paged_kv_amd/csrc/mla_kernels.h"]
+KERNEL_SOURCES = ["mla_paged_kv_amd/csrc/mla_splitkv_kernel.h", "mla_paged_kv_amd/csrc/mla_splitkv.hip",
+                  "mla_paged_kv_amd/csrc/mla_kernels.h"]
 
 
 def kernel_hash() -> str:
@@ -273,7 +274,7 @@ def prefill_work(case) -> dict:
     return dict(flop=flop, bytes=byts, kv_bytes=case["s_kv"] * d_qk * 2, keys=valid)
 
 
-def bench_prefill(steps: int, warmup: int) -> dict:
+def bench_prefill(steps: int, warmup: int, probe: bool = False) -> dict:
     """The sparse prefill chunk: one mla_sparse_prefill call per step."""
     import torch
 
@@ -299,6 +300,8 @@ def bench_prefill(steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    if probe:
+        copy_probe(torch, dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -308,6 +311,8 @@ def bench_prefill(steps: int, warmup: int) -> dict:
     ms = e0.elapsed_time(e1) / steps
     tflops = work["flop"] / (ms * 1e-3) / 1e12
     return dict(workload=case["name"], ms_per_step=round(ms, 5), tflops=round(tflops, 2),
+                kernels_ms={"splitkv+combine": round(ms, 5)},
+                algorithmic={"flop": work["flop"], "bytes": work["bytes"]},
                 roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS,
                               unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None),
                 schedule=dict(num_parts=meta.num_parts, row_blocks=meta.row_blocks,
@@ -372,8 +377,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="seeded workload (2 = varlen decode, h_q=128: the headline)")
+    ap.add_argument("--workload", default="2", choices=["1", "2", "3", "4", "5", "4f", "5f", "p"],
+                    help="seeded workload (2 = varlen decode, h_q=128: the headline; 4f/5f: "
+                         "FP8-cache variants of 4/5; p: the sparse prefill chunk)")
     ap.add_argument("--others", default="3,4,5,4f,5f,p",
                     help="extra workloads timed into 'other_workloads' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -400,9 +406,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    r = bench_workload(args.workload, args.steps, args.warmup, probe=args.copy_probe)
+    if args.workload == "p":  # the prefill chunk alone (profiling runs)
+        o = bench_prefill(args.steps, args.warmup, probe=args.copy_probe)
+        o["roofline"]["traffic"] = load_traffic("p")
+        print(json.dumps(dict(o, kernel_source_hash=kernel_hash())), flush=True)
+        return
+    k = int(args.workload) if args.workload.isdigit() else args.workload
+    r = bench_workload(k, args.steps, args.warmup, probe=args.copy_probe)
     case = r["case"]
-    r["roofline"]["traffic"] = load_traffic(args.workload)
+    r["roofline"]["traffic"] = load_traffic(k)
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),
@@ -440,6 +452,7 @@ def main():
             continue
         if k == "p":
             others["p"] = bench_prefill(max(10, args.steps // 5), 3)
+            others["p"]["roofline"]["traffic"] = load_traffic("p")
             torch.cuda.empty_cache()
             continue
         o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2))
