@@ -21,9 +21,9 @@ Algorithmic work (what the method must do, not padded work):
 The split workspace traffic is overhead and is not counted.
 
 Prints one JSON line.  The step time is the whole decode (split-KV then
-combine) timed back to back between HIP events; the per-kernel durations come
-from HIP events around runs of each kernel alone over the same number of
-launches, recorded on the stream the kernels run on.
+combine) timed back to back between two HIP events; the per-kernel durations
+come from a second pass over the same steps with HIP events before, between
+and after the two kernels of every step, recorded on the stream they run on.
 """
 from __future__ import annotations
 
@@ -213,20 +213,19 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / steps
 
-    # each kernel alone over the same number of launches, between two events
-    # on the stream the kernels run on (torch's current stream)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    ev[0].record()
+    # the same steps again with an event before, between and after the two
+    # kernels of every step (on the stream they run on): per-kernel durations
+    # in the context of the step, the launches rocprofv3 also averages over
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
+        ev[i][0].record()
         split(kvs[i % copies], meta)
-    ev[1].record()
-    ev[2].record()
-    for i in range(steps):
+        ev[i][1].record()
         combine(meta)
-    ev[3].record()
+        ev[i][2].record()
     torch.cuda.synchronize()
-    split_ms = ev[0].elapsed_time(ev[1]) / steps
-    comb_ms = ev[2].elapsed_time(ev[3]) / steps
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
 
     # rate with the scheduler and its upload inside every step
     torch.cuda.synchronize()
