@@ -701,12 +701,18 @@ void mla_splitkv(SplitKVParams p) {
     const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
     float psum = 0.f;
     s16x8 pk[2];  // this lane's P^T operand: scores 8c .. 8c+7
+    float pe[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float pe = fast_exp2(__builtin_fmaf(st[0][v], p.scale_log2, neg_m));
-      psum += pe;
-      pk[v >> 3][v & 7] = (short)f2e<F16>(pe);
+      pe[v] = fast_exp2(__builtin_fmaf(st[0][v], p.scale_log2, neg_m));
+      pk[v >> 3][v & 7] = (short)f2e<F16>(pe[v]);
     }
+    // the row sum as a pairwise tree (short dependency chain)
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int v = 0; v < w; ++v) pe[v] += pe[v + w];
+    psum = pe[0];
     // exchange P halves and row sums with the pair partner
     const float own = xor32_sum(psum);
     x_p[128 * wave + xl] = pk[0];
@@ -787,8 +793,8 @@ void mla_splitkv(SplitKVParams p) {
   // first tile: gathered into buf_a before the stream starts
   Tile ct = first_tile_from(cs0);
   uint64_t cmask;
+  const TileMeta m0 = fetch_meta(ct.u, ct.blk);
   {
-    const TileMeta m0 = fetch_meta(ct.u, ct.blk);
     if (!SPARSE) n_vis = visible(m0.len);
     qrow = row_index(ct.u, row);
     load_q(ct.u);
@@ -809,8 +815,12 @@ void mla_splitkv(SplitKVParams p) {
   // of the tile into a full drain.
   Tile nt = next_tile(ct);
   Tile n2t = next_tile(nt);
-  TileMeta nmeta{0, 0, -1}, n2meta{0, 0, -1};
+  // Past the last tile the metadata repeats the last real tile's, so the
+  // unused loads of the last step read a page this workgroup just read
+  // (rather than every workgroup reading page 0 at once).
+  TileMeta nmeta = m0, n2meta = m0;
   if (nt.s < seg_end) nmeta = fetch_meta(nt.u, nt.blk);
+  n2meta = nmeta;
   if (n2t.s < seg_end) n2meta = fetch_meta(n2t.u, n2t.blk);
 
   // One step computes the tile in `cur_buf` while the next one streams into
@@ -827,8 +837,9 @@ void mla_splitkv(SplitKVParams p) {
     wait_vmem();
     __syncthreads();
     const bool has_next = nt.s < seg_end;
-    // Without a next tile (or a valid index in it) the slices load page 0 /
-    // cache row 0 instead: harmless, in bounds and branch-free.
+    // Without a next tile the slices load page 0 (or, sparse, the zero row)
+    // instead: harmless, in bounds and branch-free (a branch per slice costs
+    // the QK loop its schedule).
     nx_plan = plan_gather(nt.blk, nmeta);
     const uint64_t nmask = has_next ? nx_plan.vmask : 0;
     nx_dst = nxt_buf;
@@ -851,6 +862,10 @@ void mla_splitkv(SplitKVParams p) {
 #pragma unroll
       for (int i = 0; i < NLW; ++i) gather_slice(i);
     }
+    // The last step: its (unused) tile loads finished during the compute;
+    // waiting for them here, before the output stores, lets the workgroup end
+    // without waiting for those stores (no load into LDS outlives it).
+    if (!has_next) wait_vmem();
     if (ct.last) {
       write_segment(qrow, seg_slot(ct.s), false);
       const int e_end = has_next ? nt.s : seg_end;
@@ -864,7 +879,7 @@ void mla_splitkv(SplitKVParams p) {
     }
     if (!has_next) return false;
     const Tile n3t = next_tile(n2t);
-    TileMeta n3meta{0, 0, -1};
+    TileMeta n3meta = n2meta;
     if (n3t.s < seg_end) n3meta = fetch_meta(n3t.u, n3t.blk);
     ct = nt;
     cmask = nmask;
@@ -885,7 +900,7 @@ void mla_splitkv(SplitKVParams p) {
       if (!step(buf_b, buf_a)) break;
     }
   }
-  wait_vmem();  // no load into LDS outlives the workgroup
+  // (the last step waited for its tile loads before its output stores)
 #endif
 }
 
