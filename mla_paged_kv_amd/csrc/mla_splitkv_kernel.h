@@ -97,6 +97,11 @@ __device__ __forceinline__ unsigned short f2e(float x) {
     return f2bf(x);
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// waits until at most N of this wave's vector memory operations are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS (and
 // scalar) accesses, not for the tile gathers still in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -401,6 +406,31 @@ void mla_splitkv(SplitKVParams p) {
 #pragma unroll
     for (int i = 0; i < NLW; ++i) gather_one(g, dst, i, lane);
   };
+  // The workgroup's 64 query rows, when they are consecutive rows of q,
+  // gathered like a dense tile (same LDS layout and swizzle; rows past the
+  // last one repeat it): 1 KB per load instead of 32-byte pieces of 32 rows
+  // per wavefront load, and each row fetched once rather than by both
+  // wavefronts of its pair.
+  auto gather_q = [&](int u, uint8_t* dst) __attribute__((always_inline)) {
+    const int r0 = rb * kRowsPerGroup;
+    const int tmax = p.rows - 1 - r0 < kRowsPerGroup - 1 ? p.rows - 1 - r0 : kRowsPerGroup - 1;
+    const uint16_t* base = p.q + row_index(u, r0) * D_QK;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
+                                                      kRowsPerGroup * RSB, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int q0 = 64 * i;
+      const int tl = q0 / CPR;
+      const int bnd = (tl + 1) * CPR - q0;
+      const bool second = bnd < 64 && lane >= bnd;
+      const int f16 = 16 * (second ? swz<CPR>(tl + 1) : swz<CPR>(tl));
+      const int n = NLW * wave + i;
+      const int t = 16 * wave + tl + (second ? 1 : 0);
+      int off = (n * 1024 + lane * 16) ^ f16;
+      if (t > tmax) off -= (t - tmax) * RSB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + n * 1024), 16, off, 0, 0, 0);
+    }
+  };
   // FP8 tile: the 64 raw rows, back to back, in 41 loads of 1 KB; wavefront w
   // issues loads w, w + 4, ...  Lane chunk q of the tile is chunk q % 41 of
   // tile row q / 41.  Rows are clamped / substituted as for bf16 tiles.  The
@@ -510,6 +540,15 @@ void mla_splitkv(SplitKVParams p) {
     const uint16_t* qp = p.q + row_index(u, row_ok ? row : p.rows - 1) * D_QK + 8 * lgrp;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+  };
+  // this wavefront's query fragments (rows 32 rgrp + lrow, the B operand of
+  // QK) from a gathered query tile: the K-operand addressing moved to the
+  // pair's rows
+  auto read_q = [&](const uint8_t* src) __attribute__((always_inline)) {
+    const int dq = (rgrp - half) * kRows * RSB;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(src + kbase[kk % NKB] + dq + kk * 32);
   };
   // The accumulator is not cleared here: the segment's first computed tile
   // starts its PV product from zero instead, so acc is only ever touched by
@@ -625,14 +664,20 @@ void mla_splitkv(SplitKVParams p) {
     if (next_q_unit >= 0) load_q(next_q_unit);
 
     // V^T fragments, prefetched PD (k-step, column-tile) steps ahead; the
-    // first PD are issued before the softmax so their latency hides behind it
+    // first PD are issued before the softmax so their latency hides behind it.
+    // PV runs its k-steps in the order e = 0..3 where e = 0, 1 cover this
+    // half's own 32 tokens (P on hand after the softmax) and e = 2, 3 the
+    // partner's (P read after the exchange): token block 16 e + 32 half for
+    // e < 2, 16 (e - 2) + 32 (1 - half) after.
     constexpr int PD = 6;
     s16x4 vf[PD + 1][2];
+    const int vsh_own = half * 32 * RSB, vsh_oth = (1 - half) * 32 * RSB;
     auto load_v = [&](int i) __attribute__((always_inline)) {
-      const int kc = i / NCT, ct = i % NCT;
+      const int e = i / NCT, ct = i % NCT;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint8_t* a = buf + vbase[h][ct % NVB] + kc * 16 * RSB + ct * 64;
+        const uint8_t* a = buf + vbase[h][ct % NVB] + (e < 2 ? vsh_own : vsh_oth) +
+                           (e & 1) * 16 * RSB + ct * 64;
         vf[i % (PD + 1)][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
       }
     };
@@ -699,47 +744,65 @@ void mla_splitkv(SplitKVParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);
     const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
-    float psum = 0.f;
     s16x8 pk[2];  // this lane's P^T operand: scores 8c .. 8c+7
     float pe[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      pe[v] = fast_exp2(__builtin_fmaf(st[0][v], p.scale_log2, neg_m));
+    // the score goes through an opaque copy: the two copies of the PV loop
+    // (first tile of a segment or not) would otherwise share their
+    // exponentials, hoisted out of both loops ahead of the MFMAs
+    auto expo = [&](int v) __attribute__((always_inline)) {
+      float sv = st[0][v];
+      asm volatile("" : "+v"(sv));
+      pe[v] = fast_exp2(__builtin_fmaf(sv, p.scale_log2, neg_m));
       pk[v >> 3][v & 7] = (short)f2e<F16>(pe[v]);
-    }
-    // the row sum as a pairwise tree (short dependency chain)
+    };
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int v = 0; v < w; ++v) pe[v] += pe[v + w];
-    psum = pe[0];
-    // exchange P halves and row sums with the pair partner
-    const float own = xor32_sum(psum);
+    for (int v = 0; v < 8; ++v) expo(v);
     x_p[128 * wave + xl] = pk[0];
-    x_p[128 * wave + 64 + xl] = pk[1];
-    if (lane < 32) x_sum[32 * wave + xl] = own;
-    lds_barrier();
-    s16x8 pp[2];
-    pp[0] = x_p[128 * (wave ^ 1) + xl];
-    pp[1] = x_p[128 * (wave ^ 1) + 64 + xl];
-    const float other = x_sum[32 * (wave ^ 1) + (xl & 31)];
-    l_part += half == 0 ? own + other : other + own;  // same sum in both halves
     __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T . P^T; PV k-steps 0,1 cover tokens 0..31 (half 0's scores)
-    // and 2,3 tokens 32..63 (half 1's)
+    // O^T += V^T . P^T.  Between the MFMAs of the own k-steps go the other
+    // half of the exponentials, the row sum (a pairwise tree, short
+    // dependency chain) and the exchange writes; the exchange barrier comes
+    // two MFMAs before the partner's P is needed.
     auto pv = [&](bool from_zero) __attribute__((always_inline)) {
+      s16x8 pp[2];
+      float own = 0.f, other = 0.f;
 #pragma unroll
       for (int i = 0; i < NSTEP; ++i) {
         if (i + PD < NSTEP) load_v(i + PD);
-        const int kc = i / NCT, ct = i % NCT;
+        const int e = i / NCT, ct = i % NCT;
         const s16x4 lo = vf[i % (PD + 1)][0], hi = vf[i % (PD + 1)][1];
         const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const s16x8 pb = (kc >> 1) == half ? pk[kc & 1] : pp[kc & 1];
-        const f32x16 c_in = (from_zero && kc == 0) ? f32x16{} : acc[ct];
+        const s16x8 pb = e < 2 ? pk[e] : pp[e - 2];
+        const f32x16 c_in = (from_zero && e == 0) ? f32x16{} : acc[ct];
         acc[ct] = mfma<F16>(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pb), c_in);
+        static_assert(NCT == 8, "one exponential per MFMA of the first k-step");
+        if (i < NCT) expo(8 + i);
+        if (i == NCT - 1) x_p[128 * wave + 64 + xl] = pk[1];
+        if (i == NCT) {
+#pragma unroll
+          for (int v = 0; v < 8; ++v) pe[v] += pe[v + 8];
+        }
+        if (i == NCT + 1) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) pe[v] += pe[v + 4];
+        }
+        if (i == NCT + 2) {
+#pragma unroll
+          for (int v = 0; v < 2; ++v) pe[v] += pe[v + 2];
+          own = xor32_sum(pe[0] + pe[1]);
+        }
+        if (i == NCT + 3 && lane < 32) x_sum[32 * wave + xl] = own;
+        if (i == 2 * NCT - 3) {
+          // exchange P halves and row sums with the pair partner
+          lds_barrier();
+          pp[0] = x_p[128 * (wave ^ 1) + xl];
+          pp[1] = x_p[128 * (wave ^ 1) + 64 + xl];
+          other = x_sum[32 * (wave ^ 1) + (xl & 31)];
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
+      l_part += half == 0 ? own + other : other + own;  // same sum in both halves
     };
     if (seg_first) {
       pv(true);
@@ -795,17 +858,38 @@ void mla_splitkv(SplitKVParams p) {
   uint64_t cmask;
   const TileMeta m0 = fetch_meta(ct.u, ct.blk);
   {
-    if (!SPARSE) n_vis = visible(m0.len);
     qrow = row_index(ct.u, row);
-    load_q(ct.u);
+    // The first segment's queries go through LDS when the workgroup's rows
+    // are consecutive rows of q (always, except for a dense call with fewer
+    // heads than h_q and several query tokens), staged in the buffer the
+    // first step gathers into (bf16) or dequantizes into (FP8).
+    const bool q_lds = SPARSE || p.heads == p.h_q || p.s_q == 1;
+    uint8_t* const q_stage = FP8 ? buf_a : buf_b;
+    if (q_lds)
+      gather_q(ct.u, q_stage);
+    else
+      load_q(ct.u);
+    if (!SPARSE) n_vis = visible(m0.len);
     reset_state();
     const Gather g0 = plan_gather(ct.blk, m0);
     cmask = g0.vmask;
-    if (!SPARSE || !WIDE || cmask != 0) {
+    const bool g0_issued = !SPARSE || !WIDE || cmask != 0;
+    if (g0_issued) {
       if constexpr (FP8)
         gather_fp8(g0, stg_a);
       else
         gather_all(g0, buf_a);
+    }
+    if (q_lds) {
+      // the query loads were issued before the tile's, which stay in flight
+      // (an FP8 tile is 10 or 11 loads per wavefront)
+      if (g0_issued)
+        wait_vmem_n<FP8 ? SNL / kWaves : NLW>();
+      else
+        wait_vmem();
+      lds_barrier();
+      read_q(q_stage);
+      lds_barrier();  // every wavefront has its queries before the buffer is reused
     }
   }
   // Tile j+1 is gathered during step j; metadata runs two tiles ahead of the
