@@ -86,12 +86,18 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
     float ls[kUnroll];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
+      // only existing splits are read (the test is uniform over the
+      // wavefront); the others get weight 0 below
       const int s = s0 + j * kStride;
-      const int sl = s < nsplit ? s : s0;  // in-bounds stand-in, weight 0 below
-      ls[j] = lse_col[size_t(sl) * p.rows];
-      const float* src = o_col + size_t(sl) * split_stride;
-      v0[j] = *reinterpret_cast<const f32x4*>(src);
-      v1[j] = *reinterpret_cast<const f32x4*>(src + 4);
+      ls[j] = -__builtin_inff();
+      v0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s < nsplit) {
+        ls[j] = lse_col[size_t(s) * p.rows];
+        const float* src = o_col + size_t(s) * split_stride;
+        v0[j] = *reinterpret_cast<const f32x4*>(src);
+        v1[j] = *reinterpret_cast<const f32x4*>(src + 4);
+      }
     }
     float mb = m;
 #pragma unroll
