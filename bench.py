@@ -201,31 +201,50 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     if probe:
         copy_probe(torch, dev)
 
-    # whole decode steps (split-KV then combine), back to back
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(steps):
-        split(kvs[i % copies], meta)
-        combine(meta)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / steps
+    # The timed loops run as HIP-graph replays (torch.cuda.CUDAGraph over the
+    # library's launches, captured once, default-priority stream): no host
+    # work between the kernels, as in a serving loop that captures its decode
+    # step.  Each graph holds exactly `steps` iterations; it is replayed once
+    # untimed, then once between two events.
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        torch.cuda.synchronize()
+        return g
 
-    # the same steps again with an event before, between and after the two
-    # kernels of every step (on the stream they run on): per-kernel durations
-    # in the context of the step, the launches rocprofv3 also averages over
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        split(kvs[i % copies], meta)
-        ev[i][1].record()
-        combine(meta)
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    def replay_ms(g):
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def steps_body():
+        for i in range(steps):
+            split(kvs[i % copies], meta)
+            combine(meta)
+
+    def combine_body():
+        for _ in range(steps):
+            combine(meta)
+
+    # whole decode steps (split-KV then combine), back to back
+    g_step = capture(steps_body)
+    ms_step = replay_ms(g_step)
+    # per-kernel durations.  An event recorded between the two kernels of a
+    # step adds a dispatch gap of several microseconds to both intervals, and
+    # split-KV launches back to back with nothing between them run slower
+    # than in the step loop.  So the combine is timed alone (`steps` launches
+    # back to back) and the split-KV kernel is the whole step minus that:
+    # the durations rocprofv3 reports for the launches of the step loop.
+    g_comb = capture(combine_body)
+    comb_ms = replay_ms(g_comb)
+    split_ms = ms_step - comb_ms
+    del g_step, g_comb
 
     # rate with the scheduler and its upload inside every step
     torch.cuda.synchronize()

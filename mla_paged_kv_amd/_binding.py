@@ -153,6 +153,14 @@ class Metadata:
         o = int(m[12])
         return m[o:o + 4 * int(m[1])].reshape(-1, 4)
 
+    def blocks_needed(self) -> int:
+        """Most block-table columns any segment reaches (host-built metadata;
+        computed once)."""
+        if getattr(self, "_blocks_needed", None) is None:
+            segs = self.segments
+            self._blocks_needed = int(segs[:, 2].max()) if len(segs) else 0
+        return self._blocks_needed
+
     def workspace_bytes(self, dv: int = 512) -> int:
         return int(_load().mla_workspace_bytes(ctypes.byref(self.info), dv))
 
@@ -323,8 +331,7 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
     _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
     _need(cache_seqlens.shape == (B,), "cache_seqlens must be [B]")
     if not meta.device_built:  # (device metadata is not read back: no synchronisation)
-        segs = meta.segments
-        _need(len(segs) == 0 or int(segs[:, 2].max()) <= block_table.shape[1],
+        _need(meta.blocks_needed() <= block_table.shape[1],
               "cache_seqlens of the metadata need more blocks than block_table has columns")
     if softmax_scale is None:
         softmax_scale = d_qk ** -0.5
