@@ -24,7 +24,7 @@ Definitions followed (citations name the page, then the section):
   cache, ``-1`` invalid, no block table (upstream README, "Sparse Attention
   (indices tensor)").
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * LSE is the natural log of the summed exp of the *scaled* scores.  (The
   sparse-prefill equations use base 2 with scores pre-multiplied by log2(e);

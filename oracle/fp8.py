@@ -11,8 +11,7 @@ flashmla-optimization page, "FP8 KV Cache"): 656 bytes per token,
 
 The kernel dequantizes the cache to bfloat16 and computes attention in
 bfloat16 (same section).  The pages do not spell out the e4m3 encoding or the
-rounding of the dequantized value; the readings taken here (listed in the
-design notes):
+rounding of the dequantized value; the readings taken here:
 
 * e4m3 is the OCP 8-bit "E4M3" encoding as PyTorch's ``float8_e4m3fn``: 1 sign
   bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes

@@ -12,7 +12,7 @@ is equivalent to): for query token i with its top-k KV rows K_i = kv[indices[i]]
     S          = 2^(P - lse)
     out        = S @ K_i                                  [h_q, d_v]
 
-Readings taken where the page is silent (listed in the design notes):
+Readings taken where the page is silent:
 
 * Invalid entries (-1 or >= s_kv, the page's rule) are left out of every sum
   and maximum; a query whose entries are all invalid gets out = 0 and

@@ -188,7 +188,7 @@ def make_prefill_case(seed: int, *, s_q: int, s_kv: int, h_q: int, topk: int, d_
 # Sparse prefill: one 4096-token chunk over a 32768-token context, every query
 # with its own top-2048 positions (DeepSeek-style sparse attention shapes: 128
 # heads, 576-wide latent rows).
-PREFILL_CONFIG = dict(name="sparse prefill: s_q=4096 s_kv=32768 h_q=128 d_qk=576 d_v=512 topk 2048",
+PREFILL_WORKLOAD = dict(name="sparse prefill: s_q=4096 s_kv=32768 h_q=128 d_qk=576 d_v=512 topk 2048",
                       s_q=4096, s_kv=32768, h_q=128, topk=2048)
 
 
@@ -196,7 +196,7 @@ def _c2_lens(rng):
     return rng.integers(1, 4097, size=64)
 
 
-def _c4_lens(rng):
+def _skewed_long_lens(rng):
     lo, hi = math.log(32768), math.log(131072)
     long = np.floor(np.exp(rng.uniform(lo, hi, size=8))).astype(np.int64)
     long = np.clip(long, 32768, 131072)
@@ -204,7 +204,7 @@ def _c4_lens(rng):
     return np.concatenate([long, short])
 
 
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="tiny: B=2 s_q=1 h_q=16 seqlens {64,200} pool 8",
             kind="dense", B=2, s_q=1, h_q=16, seqlens=[64, 200], table_width=4,
             reshape_table=True),
@@ -215,7 +215,7 @@ CONFIGS = {
             kind="dense", B=128, s_q=2, h_q=128, seqlens=[4096] * 128, causal=True,
             table_width=64),
     4: dict(name="skewed long context: B=16 s_q=1 h_q=64, 8 x logU[32k,128k] + 8 x U[1,256]",
-            kind="dense", B=16, s_q=1, h_q=64, seqlen_sampler=_c4_lens, table_width=2048),
+            kind="dense", B=16, s_q=1, h_q=64, seqlen_sampler=_skewed_long_lens, table_width=2048),
     5: dict(name="top-k sparse: B=32 s_q=1 h_q=64 (16 active) d_qk=d_v=512 topk 2048, 102 invalid",
             kind="sparse", B=32, s_q=1, h_q=64, active_h_q=16, topk=2048, cache_len=65536,
             invalid_tail=102, d_qk=512, d_v=512),
@@ -224,10 +224,10 @@ CONFIGS = {
 
 # The same shapes with an FP8-with-scale cache (576-wide rows: the format holds
 # 512 + 64 values), seed 1000 + k as for the bf16 workload they follow.
-FP8_CONFIGS = {
-    "4f": dict(CONFIGS[4], name="skewed long context, FP8 cache: B=16 s_q=1 h_q=64, "
+FP8_WORKLOADS = {
+    "4f": dict(WORKLOADS[4], name="skewed long context, FP8 cache: B=16 s_q=1 h_q=64, "
                                 "8 x logU[32k,128k] + 8 x U[1,256]", kv_fp8=True),
-    "5f": dict(CONFIGS[5], name="top-k sparse, FP8 cache: B=32 s_q=1 h_q=64 (16 active) "
+    "5f": dict(WORKLOADS[5], name="top-k sparse, FP8 cache: B=32 s_q=1 h_q=64 (16 active) "
                                 "d_qk=576 d_v=512 topk 2048, 102 invalid", d_qk=576, kv_fp8=True),
 }
 
@@ -236,13 +236,13 @@ def make_config(k) -> dict:
     """The five named workloads (k = 1..5), seed 1000 + k, their FP8-cache
     variants ("4f", "5f") and the sparse prefill chunk ("p", seed 1100)."""
     if k == "p":
-        return make_prefill_case(1100, **PREFILL_CONFIG)
-    if isinstance(k, str) and k in FP8_CONFIGS:
-        spec = dict(FP8_CONFIGS[k])
+        return make_prefill_case(1100, **PREFILL_WORKLOAD)
+    if isinstance(k, str) and k in FP8_WORKLOADS:
+        spec = dict(FP8_WORKLOADS[k])
         seed = 1000 + int(k[:-1])
     else:
         k = int(k)
-        spec = dict(CONFIGS[k])
+        spec = dict(WORKLOADS[k])
         seed = 1000 + k
     kind = spec.pop("kind")
     name = spec.pop("name")

@@ -74,8 +74,8 @@ def test_cpp_scheduler_bit_exact_vs_reference(lib, lens, P, rows):
 
 
 def test_cpp_scheduler_bit_exact_at_config_shapes(lib):
-    from synth.configs import CONFIGS, rng_for
-    for k, spec in CONFIGS.items():
+    from synth.configs import WORKLOADS, rng_for
+    for k, spec in WORKLOADS.items():
         if spec["kind"] == "dense":
             lens = spec.get("seqlens")
             if lens is None:

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import mla_paged_kv_amd as mla
-from synth.configs import CONFIGS, _c4_lens, make_dense_case, make_sparse_case
+from synth.configs import WORKLOADS, _skewed_long_lens, make_dense_case, make_sparse_case
 from tests._gpu_util import compare, log, metadata, run_gpu, run_oracle, to_device, to_np
 
 pytestmark = pytest.mark.gpu
@@ -133,8 +133,8 @@ def test_fp8_pages_call_shape():
 
 
 def test_fp8_skewed_long_context_full_size():
-    spec = dict(CONFIGS[4])
-    case = make_dense_case(1004, B=16, s_q=1, h_q=64, seqlen_sampler=_c4_lens, table_width=2048,
+    spec = dict(WORKLOADS[4])
+    case = make_dense_case(1004, B=16, s_q=1, h_q=64, seqlen_sampler=_skewed_long_lens, table_width=2048,
                            kv_fp8=True)
     log(f"fp8 skewed long context: {spec['name']}")
     _check(case, num_parts=0, batches=[0, 3, 7, 8, 12, 15], what="fp8 skewed long context")
