@@ -241,10 +241,13 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     # than in the step loop.  So the combine is timed alone (`steps` launches
     # back to back) and the split-KV kernel is the whole step minus that:
     # the durations rocprofv3 reports for the launches of the step loop.
-    g_comb = capture(combine_body)
-    comb_ms = replay_ms(g_comb)
+    comb_ms = 0.0
+    if meta.num_split_units > 0:  # else the combine launches nothing
+        g_comb = capture(combine_body)
+        comb_ms = replay_ms(g_comb)
+        del g_comb
     split_ms = ms_step - comb_ms
-    del g_step, g_comb
+    del g_step
 
     # rate with the scheduler and its upload inside every step
     torch.cuda.synchronize()
