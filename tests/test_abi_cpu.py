@@ -259,3 +259,121 @@ def test_workspace_bytes(lib):
     assert n == -(-slots * rows * 512 * 4 // 256) * 256 + 2 * (-(-slots * rows * 4 // 256) * 256)
     rc, meta, info = _raw_meta(lib, [64, 64], P=2, rows=16)
     assert info.total_slots == 0 and lib.mla_workspace_bytes(ctypes.byref(info), 512) == 0
+
+
+def _sparse_meta(lib, units, heads=16, topk=2048, P=8):
+    cap = lib.mla_metadata_capacity(units, P)
+    meta = np.zeros(cap, dtype=np.int32)
+    info = B.MlaSchedInfo()
+    assert lib.mla_get_metadata(None, units, 1, 64, 1, topk, heads, 0, P, meta.ctypes.data, cap,
+                                ctypes.byref(info)) == 0
+    return meta, info
+
+
+@pytest.mark.parametrize("name", ["mla_sparse_prefill", "mla_sparse_prefill_f16"])
+def test_sparse_prefill_rejects_bad_arguments(lib, name):
+    meta, info = _sparse_meta(lib, 3)
+    ws = lib.mla_workspace_bytes(ctypes.byref(info), 512)
+
+    def call(**kw):
+        a = dict(q=FAKE, kv=FAKE, ix=FAKE, s_q=3, s_kv=4096, h_q=64, h_kv=1, d_qk=576, dv=512,
+                 topk=2048, scale=0.04, ws=FAKE, ws_bytes=ws, out=FAKE, ml=FAKE, lse=FAKE)
+        a.update(kw)
+        return getattr(lib, name)(a["q"], a["kv"], a["ix"], a["s_q"], a["s_kv"], a["h_q"],
+                                  a["h_kv"], a["d_qk"], a["dv"], a["topk"], a["scale"], FAKE,
+                                  ctypes.byref(info), a["ws"], a["ws_bytes"], a["out"], a["ml"],
+                                  a["lse"], None)
+
+    assert call(s_kv=0) == -1
+    assert call(s_kv=-5) == -1
+    assert call(s_kv=(1 << 31) - 1) == -1                   # rows would overflow int32
+    assert call(ix=None) == -1
+    assert call(topk=0) == -1
+    assert call(scale=0.0) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(ml=FAKE + 2) == -1                          # max_logits misaligned
+    assert call(s_q=2) == -1                                # metadata built for 3 query tokens
+    assert b"units" in lib.mla_last_error()
+    assert call(h_q=8) == -1                                # 16 active heads > h_q
+    assert call(h_kv=2) == -2
+    assert call(d_qk=576, dv=576) == -2
+    assert call(ws_bytes=ws - 4) == -3
+    assert call(ws=FAKE + 64) == -1                         # workspace not 256-aligned
+    assert call(q=None) == -1
+    assert call(lse=FAKE + 1) == -1
+    assert call(s_q=0) == 0                                 # empty: nothing to launch
+
+
+@pytest.mark.parametrize("suffix", ["", "_f16", "_fp8"])
+def test_decode_variants_share_the_checks(lib, suffix):
+    rc, meta, info = _raw_meta(lib, [64, 200], P=512, rows=16)
+    ws = lib.mla_workspace_bytes(ctypes.byref(info), 512)
+    for stage in ("decode", "splitkv"):
+        fn = getattr(lib, f"mla_{stage}_paged{suffix}")
+        args = [FAKE, FAKE, FAKE, FAKE, 2, 1, 16, 1, 576, 512, 8, 64, 4, 0, 0.04, FAKE,
+                ctypes.byref(info), FAKE, ws, FAKE, FAKE, None]
+        bad = list(args)
+        bad[11] = 32                                        # page size
+        assert fn(*bad) == -2
+        bad = list(args)
+        bad[4] = 3                                          # metadata for 2 units
+        assert fn(*bad) == -1
+        bad = list(args)
+        bad[18] = ws - 1
+        assert fn(*bad) == -3
+        bad = list(args)
+        bad[8], bad[4] = 512, 0   # d_qk 512, empty batch: the FP8 format needs 576, else no-op
+        assert fn(*bad) == (-2 if suffix == "_fp8" else 0)
+    smeta, sinfo = _sparse_meta(lib, 2)
+    sws = lib.mla_workspace_bytes(ctypes.byref(sinfo), 512)
+    for stage in ("decode", "splitkv"):
+        fn = getattr(lib, f"mla_{stage}_sparse{suffix}")
+        args = [FAKE, FAKE, FAKE, 2, 1, 64, 1, 576, 512, 64, 64, 2048, 0.04, FAKE,
+                ctypes.byref(sinfo), FAKE, sws, FAKE, FAKE, None]
+        bad = list(args)
+        bad[2] = None                                       # indices
+        assert fn(*bad) == -1
+        bad = list(args)
+        bad[11] = 0                                         # topk
+        assert fn(*bad) == -1
+        bad = list(args)
+        bad[7] = 512
+        bad[3] = 0
+        assert fn(*bad) == (-2 if suffix == "_fp8" else 0)
+
+
+@pytest.mark.parametrize("name", ["mla_combine", "mla_combine_f16"])
+def test_combine_rejects_bad_arguments(lib, name):
+    fn = getattr(lib, name)
+    rc, meta, info = _raw_meta(lib, [64, 200], P=512, rows=16)
+    assert info.num_split_units > 0
+    ws = lib.mla_workspace_bytes(ctypes.byref(info), 512)
+
+    def call(pinfo=None, **kw):
+        a = dict(meta=FAKE, batch=2, s_q=1, h_q=16, dv=512, sparse=0, ws=FAKE, ws_bytes=ws,
+                 out=FAKE, lse=FAKE)
+        a.update(kw)
+        return fn(a["meta"], pinfo if pinfo is not None else ctypes.byref(info), a["batch"],
+                  a["s_q"], a["h_q"], a["dv"], a["sparse"], a["ws"], a["ws_bytes"], a["out"],
+                  a["lse"], None)
+
+    assert fn(FAKE, None, 2, 1, 16, 512, 0, FAKE, ws, FAKE, FAKE, None) == -1   # null info
+    assert call(dv=256) == -2
+    assert call(sparse=2) == -1
+    assert call(s_q=0) == -1
+    assert call(batch=3) == -1                  # metadata for 2 units
+    assert call(s_q=3) == -1                    # rows 16 not a multiple of 3
+    assert call(h_q=8) == -1                    # 16 heads > h_q
+    assert call(sparse=1, s_q=2) == -1          # sparse: 2 units != batch*s_q = 4
+    assert call(ws=None) == -1
+    assert call(ws=FAKE + 16) == -1             # not 256-aligned
+    assert call(out=FAKE + 8) == -1
+    assert call(ws_bytes=ws - 1) == -3
+    assert call(batch=0) == -1                  # metadata for 2 units, batch 0
+    bad = B.MlaSchedInfo.from_buffer_copy(info)
+    bad.total_ints = 1
+    assert call(pinfo=ctypes.byref(bad)) == -1
+    # metadata without split units: nothing to combine, pointers never touched
+    rc, meta1, info1 = _raw_meta(lib, [64, 64], P=2, rows=16)
+    assert info1.num_split_units == 0
+    assert fn(None, ctypes.byref(info1), 2, 1, 16, 512, 0, None, 0, None, None, None) == 0
