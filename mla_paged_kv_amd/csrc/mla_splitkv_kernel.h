@@ -119,10 +119,15 @@ __device__ __forceinline__ void swap_halves(float v, float& lo, float& hi) {
   hi = v;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
 }
+// Maximum of scores.  The NaN-propagating form maps to v_maximum3_f32 with no
+// operand quieting, where fmaxf would first canonicalize operands that the
+// compiler cannot prove are quiet.  Masked scores are -inf, never NaN; a NaN
+// among the visible scores makes the row's output NaN with either form.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float xor32_max(float v) {
   float lo, hi;
   swap_halves(v, lo, hi);
-  return fmaxf(lo, hi);
+  return smax(lo, hi);
 }
 __device__ __forceinline__ float xor32_sum(float v) {
   float lo, hi;
@@ -698,7 +703,7 @@ void mla_splitkv(SplitKVParams p) {
     float mloc = -__builtin_inff();
     if (full) {
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mloc = fmaxf(mloc, fmaxf(st[0][v], st[0][v + 1]));
+      for (int v = 0; v < 16; v += 2) mloc = smax(smax(mloc, st[0][v]), st[0][v + 1]);
     } else {
       // sparse: the lane's tokens are 32 half + 4 lgrp + c, c = tok(v, 0) <= 27,
       // so one shift of the tile mask leaves a 32-bit word tested at
@@ -716,14 +721,14 @@ void mla_splitkv(SplitKVParams p) {
         }
         const float x = vis ? st[0][v] : -__builtin_inff();
         st[0][v] = x;
-        mloc = fmaxf(mloc, x);
+        mloc = smax(mloc, x);
       }
     }
     mloc = xor32_max(mloc);
     if (lane < 32) x_max[32 * wave + xl] = mloc;  // maximum over both token halves
     lds_barrier();
-    mloc = fmaxf(mloc, x_max[32 * (wave ^ 1) + (xl & 31)]) * p.scale_log2;
-    m_exact = fmaxf(m_exact, mloc);
+    mloc = smax(mloc, x_max[32 * (wave ^ 1) + (xl & 31)]) * p.scale_log2;
+    m_exact = smax(m_exact, mloc);
     const bool grow = mloc > m_run + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? mloc : m_run;
