@@ -204,8 +204,12 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     # The timed loops run as HIP-graph replays (torch.cuda.CUDAGraph over the
     # library's launches, captured once, default-priority stream): no host
     # work between the kernels, as in a serving loop that captures its decode
-    # step.  Each graph holds exactly `steps` iterations; it is replayed once
-    # untimed, then once between two events.
+    # step.  Each graph holds exactly `steps` iterations; it is replayed
+    # untimed for at least `settle_s` seconds (a short workload's few
+    # milliseconds otherwise catch the clock still ramping up from idle),
+    # then once between two events.
+    settle_s = 0.2
+
     def capture(body):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -214,7 +218,12 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
         return g
 
     def replay_ms(g):
-        g.replay()
+        t_settle = time.perf_counter()
+        while True:
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_settle >= settle_s:
+                break
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()

@@ -642,10 +642,11 @@ void mla_splitkv(SplitKVParams p) {
     // lane offsets are recomputed per tile rather than kept live for both
     int xl = lane;
     if constexpr (FP8) asm volatile("" : "+v"(xl));
-    // S^T of this half's 32 tokens as two accumulation chains (even and odd
-    // k-steps), added at the end
+    // S^T of this half's 32 tokens, one accumulation chain over the k-steps
+    // (the matrix core accumulates back-to-back into the same registers, so a
+    // second chain would only add its read-out and 16 additions)
     constexpr int QD = 4;  // K fragments prefetched this many k-steps ahead
-    f32x16 st[2];
+    f32x16 st[1];
     bf16x8 kf[QD + 1];
     auto load_k = [&](int kk) __attribute__((always_inline)) {
       kf[kk % (QD + 1)] = *reinterpret_cast<const bf16x8*>(buf + kbase[kk % NKB] + kk * 32);
@@ -658,14 +659,12 @@ void mla_splitkv(SplitKVParams p) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + QD < KK) load_k(kk + QD);
-      const int c = kk & 1;
-      st[c] = mfma<F16>(kf[kk % (QD + 1)], qf[kk], kk < 2 ? f32x16{} : st[c]);
+      st[0] = mfma<F16>(kf[kk % (QD + 1)], qf[kk], kk < 1 ? f32x16{} : st[0]);
       // the next tile's gather, one slice every other k-step
       if constexpr (!FP8)
         if ((kk & 1) == 0 && kk / 2 < NLW) gather_slice(kk / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    st[0] += st[1];
     if (next_q_unit >= 0) load_q(next_q_unit);
 
     // V^T fragments, prefetched PD (k-step, column-tile) steps ahead; the
