@@ -332,6 +332,11 @@ def bench_prefill(steps: int, warmup: int, probe: bool = False) -> dict:
     torch.cuda.synchronize()
     if probe:
         copy_probe(torch, dev)
+    # untimed calls for at least 0.2 s first, as for the decode timings
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.2:
+        run()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
