@@ -35,16 +35,19 @@ __device__ __forceinline__ unsigned short f2bf(float x) {
 //    wavefront w merges splits w, w+4, ... and the four results are merged
 //    through LDS;
 //  * ROW_WAVES = false (at most a few splits): one wavefront per (split unit,
-//    row), four rows per workgroup, no LDS.
+//    row), four rows per workgroup, no LDS.  With at most 5 splits per unit
+//    the loads of 4 splits are issued at a time (UNROLL = 4): 56 instead of
+//    93 registers, so 8 wavefronts per SIMD instead of 5, which matters when
+//    the grid has many rows (h_q = 128: thousands of wavefronts).
 // A wavefront merges its splits against its own running maximum, issuing the
 // loads of up to kUnroll splits (their LSE and 8 partial-output columns per
 // lane) before using any, so the partial outputs are read in one round trip
 // per kUnroll splits with no separate pass over the LSEs.  Base-2
 // log-sum-exp throughout:
 //   lse = m + log2 sum_s 2^(lse_s - m),  O = sum_s 2^(lse_s - lse) O_s.
-template <bool ROW_WAVES>
+template <bool ROW_WAVES, int UNROLL>
 __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
-  constexpr int kWaves = 4, kUnroll = 8;
+  constexpr int kWaves = 4, kUnroll = UNROLL;
   constexpr int kStride = ROW_WAVES ? kWaves : 1;  // split stride of a wavefront
   __shared__ f32x4 red[ROW_WAVES ? kWaves : 1][64][2];  // per-wavefront weighted sums
   __shared__ float red_m[kWaves], red_l[kWaves];
@@ -187,11 +190,13 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   if (p.num_split_units <= 0 || p.rows <= 0) return hipSuccess;
   const dim3 block(256);
+  const dim3 rows4(p.num_split_units * ((p.rows + 3) / 4));
   if (p.max_splits > 16) {
-    hipLaunchKernelGGL(mla_combine<true>, dim3(p.num_split_units * p.rows), block, 0, stream, p);
+    hipLaunchKernelGGL((mla_combine<true, 8>), dim3(p.num_split_units * p.rows), block, 0, stream, p);
+  } else if (p.max_splits > 5) {
+    hipLaunchKernelGGL((mla_combine<false, 8>), rows4, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL(mla_combine<false>, dim3(p.num_split_units * ((p.rows + 3) / 4)), block, 0,
-                       stream, p);
+    hipLaunchKernelGGL((mla_combine<false, 4>), rows4, block, 0, stream, p);
   }
   return hipGetLastError();
 }
