@@ -41,14 +41,21 @@ sys.path.insert(0, ROOT)
 METRIC = "paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512) on 1 GPU"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-KERNEL_SOURCES = ["mla_paged_kv_amd/csrc/mla_splitkv_kernel.h", "mla_paged_kv_amd/csrc/mla_splitkv.hip",
-                  "mla_paged_kv_amd/csrc/mla_kernels.h"]
+CSRC = os.path.join(ROOT, "mla_paged_kv_amd", "csrc")
+
+
+def kernel_sources():
+    """Every source of the library: the kernels, the launchers, the host and
+    device schedulers (which set the split partial traffic) and the C ABI."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith((".h", ".hip", ".cpp")))
 
 
 def kernel_hash() -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in kernel_sources():
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

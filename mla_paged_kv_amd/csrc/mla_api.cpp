@@ -47,8 +47,11 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
   if (info->num_parts < 0 || info->row_blocks < 1 || info->rows < 1 || info->total_slots < 0 ||
       info->num_split_units < 0 || info->total_ints < kHeaderInts)
     return set_error(MLA_E_INVAL, "decode: malformed metadata header");
-  if (info->row_blocks != (info->rows + 63) / 64)
-    return set_error(MLA_E_INVAL, "decode: metadata row_blocks inconsistent");
+  {
+    const int32_t rbk = rows_per_group(info->rows);
+    if (info->row_blocks != (info->rows + rbk - 1) / rbk)
+      return set_error(MLA_E_INVAL, "decode: metadata row_blocks inconsistent");
+  }
   if (batch == 0) return MLA_OK;
   if (!q || !kvcache || !meta_dev || !out || !lse)
     return set_error(MLA_E_INVAL, "decode: null q/kvcache/meta/out/lse");
@@ -68,6 +71,15 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
 }
 
 enum { kStageSplit = 1, kStageCombine = 2 };
+
+}  // namespace
+
+hipError_t launch_decode(const SplitKVParams& p, int d_qk, bool sparse, bool f16, hipStream_t st) {
+  if (d_qk == 576) return f16 ? launch_decode_d<576, true>(p, sparse, st) : launch_decode_d<576, false>(p, sparse, st);
+  return f16 ? launch_decode_d<512, true>(p, sparse, st) : launch_decode_d<512, false>(p, sparse, st);
+}
+
+namespace {
 
 // Workspace: fp32 partial outputs [slots, rows, dv], then (256-byte aligned)
 // partial base-2 LSEs [slots, rows], then partial row maxima [slots, rows].
@@ -128,7 +140,7 @@ int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool spa
   kp.row_blocks = info->row_blocks;
   kp.rows = info->rows;
   if (stages & kStageSplit) {
-    const hipError_t e = launch_splitkv(kp, d_qk, sparse, fp8, f16, st);
+    const hipError_t e = fp8 ? launch_splitkv_fp8(kp, sparse, st) : launch_decode(kp, d_qk, sparse, f16, st);
     if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
   if (stages & kStageCombine)

@@ -54,9 +54,12 @@ struct CombineParams {
   int32_t sparse;
 };
 
-hipError_t launch_splitkv(const SplitKVParams& p, int d_qk, bool sparse, bool fp8, bool f16,
-                          hipStream_t stream);
-hipError_t launch_splitkv_f16(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream);
+// bf16 / fp16 caches (mla_decode_kernel.h), one launcher per (d_qk, type)
+template <int D_QK, bool F16>
+hipError_t launch_decode_d(const SplitKVParams& p, bool sparse, hipStream_t stream);
+hipError_t launch_decode(const SplitKVParams& p, int d_qk, bool sparse, bool f16, hipStream_t stream);
+// FP8-with-scale caches (mla_splitkv_kernel.h; 64 query rows per workgroup)
+hipError_t launch_splitkv_fp8(const SplitKVParams& p, bool sparse, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace mla

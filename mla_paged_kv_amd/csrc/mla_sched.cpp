@@ -32,7 +32,6 @@ namespace {
 
 constexpr int32_t kPage = 64;
 constexpr int32_t kOverhead = 5;      // F, per-segment overhead in blocks
-constexpr int32_t kRowsPerGroup = 64; // query rows per workgroup
 constexpr int32_t kGroupsPerCU = 1;   // resident workgroups per compute unit (LDS-bound)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -41,7 +40,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int32_t default_num_parts(int32_t rows, int32_t num_cus) {
   if (rows <= 0 || num_cus <= 0) return 1;
-  const int64_t row_blocks = ceil_div(rows, kRowsPerGroup);
+  const int64_t row_blocks = ceil_div(rows, rows_per_group(rows));
   const int64_t p = (int64_t(kGroupsPerCU) * num_cus) / row_blocks;
   return p < 1 ? 1 : int32_t(p > INT32_MAX ? INT32_MAX : p);
 }
@@ -154,7 +153,7 @@ int build_schedule(const int64_t* len, int32_t n, int32_t parts, int32_t rows,
   h.total_cost = int32_t(total);
   h.target_parts = parts;
   h.overhead = kOverhead;
-  h.row_blocks = int32_t(ceil_div(rows, kRowsPerGroup));
+  h.row_blocks = int32_t(ceil_div(rows, rows_per_group(rows)));
   h.rows = rows;
   h.off_segs = off_segs;
   h.off_num_splits = off_ns;

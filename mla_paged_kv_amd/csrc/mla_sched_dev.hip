@@ -320,7 +320,7 @@ extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int32_t
   p.topk = topk;
   p.sparse = topk > 0 ? 1 : 0;
   p.rows = sh.rows;
-  p.row_blocks = (sh.rows + 63) / 64;
+  p.row_blocks = (sh.rows + rows_per_group(sh.rows) - 1) / rows_per_group(sh.rows);
   hipLaunchKernelGGL(mla_sched_dev, dim3(1), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      p);
   const hipError_t e = hipGetLastError();

@@ -992,44 +992,23 @@ void mla_splitkv(SplitKVParams p) {
 #endif
 }
 
-// Launches the split-KV kernel for the given shape class; instantiated once
-// for bf16 (mla_splitkv.hip) and once for fp16 (mla_splitkv_f16.hip).
-template <bool F16>
-hipError_t launch_splitkv_t(const SplitKVParams& p, int d_qk, bool sparse, bool fp8,
-                            hipStream_t stream) {
-  const int groups = p.num_parts * p.row_blocks;
+// Launches the FP8-cache kernel (64 query rows per workgroup, whatever the
+// rows per workgroup the schedule was sized for: a part then spans
+// ceil(rows / 64) workgroups).
+inline hipError_t launch_splitkv_fp8_t(const SplitKVParams& p, bool sparse, hipStream_t stream) {
+  const int row_blocks = (p.rows + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int groups = p.num_parts * row_blocks;
   if (groups <= 0) return hipSuccess;
+  SplitKVParams q = p;
+  q.row_blocks = row_blocks;
   const dim3 grid(groups), block(256);
   // Sparse rows are addressed with 32-bit byte offsets while the pool (plus
   // the past-the-end row an all-invalid tile reads) fits in 32 bits.
-  const uint64_t row_bytes = fp8 ? kFp8RowBytes : uint64_t(d_qk) * 2;
-  const bool wide = (uint64_t(p.num_rows) + 2) * row_bytes > 0xFFFFFFFFull;
-  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, p); };
-  if constexpr (F16) {
-    if (d_qk == 576) {
-      if (!sparse) go(mla_splitkv<576, false, false, false, true>);
-      else if (!wide) go(mla_splitkv<576, true, false, false, true>);
-      else go(mla_splitkv<576, true, true, false, true>);
-    } else {
-      if (!sparse) go(mla_splitkv<512, false, false, false, true>);
-      else if (!wide) go(mla_splitkv<512, true, false, false, true>);
-      else go(mla_splitkv<512, true, true, false, true>);
-    }
-  } else {
-    if (fp8) {
-      if (!sparse) go(mla_splitkv<576, false, false, true, false>);
-      else if (!wide) go(mla_splitkv<576, true, false, true, false>);
-      else go(mla_splitkv<576, true, true, true, false>);
-    } else if (d_qk == 576) {
-      if (!sparse) go(mla_splitkv<576, false, false, false, false>);
-      else if (!wide) go(mla_splitkv<576, true, false, false, false>);
-      else go(mla_splitkv<576, true, true, false, false>);
-    } else {
-      if (!sparse) go(mla_splitkv<512, false, false, false, false>);
-      else if (!wide) go(mla_splitkv<512, true, false, false, false>);
-      else go(mla_splitkv<512, true, true, false, false>);
-    }
-  }
+  const bool wide = (uint64_t(p.num_rows) + 2) * uint64_t(kFp8RowBytes) > 0xFFFFFFFFull;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, q); };
+  if (!sparse) go(mla_splitkv<576, false, false, true, false>);
+  else if (!wide) go(mla_splitkv<576, true, false, true, false>);
+  else go(mla_splitkv<576, true, true, true, false>);
   return hipGetLastError();
 }
 

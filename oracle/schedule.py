@@ -41,10 +41,13 @@ parts.  A unit cut into k >= 2 segments is "split": its segments get
 consecutive workspace slots, numbered over split units in unit order; an unsplit
 unit's single segment gets slot -1 (written straight to the output).
 
-Default part count: ``rows`` query rows per unit are processed 64 per
-workgroup and one workgroup is resident per compute unit (a workgroup holds
-two 64-token cache pages in LDS, 144 KiB of the 160 KiB), so that every part
-starts at once: ``P = max(1, num_cus // ceil(rows / 64))``.
+Default part count: ``rows`` query rows per unit are processed ``G(rows)``
+per workgroup, where G(rows) = 128 if rows > 64, 64 if 32 < rows <= 64, else
+32, and one workgroup is resident per compute unit (a workgroup's tile buffers
+fill most of the LDS), so that every part starts at once:
+``row_blocks = ceil(rows / G(rows))`` and ``P = max(1, num_cus // row_blocks)``.
+G is a parameter of the specification (``rows_per_group``), not a property the
+pages fix.
 
 Metadata layout (int32):
 
@@ -63,18 +66,29 @@ import numpy as np
 
 PAGE_BLOCK = 64
 SPLIT_OVERHEAD_BLOCKS = 5
-ROWS_PER_WORKGROUP = 64
 WORKGROUPS_PER_CU = 1
 HEADER_INTS = 16
 
 
-def ref_num_parts(rows: int, num_cus: int) -> int:
-    row_blocks = -(-rows // ROWS_PER_WORKGROUP)
-    return max(1, (WORKGROUPS_PER_CU * num_cus) // row_blocks)
+def rows_per_group(rows: int) -> int:
+    """G(rows): query rows per workgroup (see the specification above)."""
+    if rows > 64:
+        return 128
+    return 64 if rows > 32 else 32
 
 
-def ref_schedule(lens, target_parts: int, rows: int) -> np.ndarray:
-    """Build the metadata array for unit lengths ``lens`` and ``target_parts`` parts."""
+def ref_row_blocks(rows: int, group=None) -> int:
+    g = rows_per_group(rows) if group is None else group
+    return -(-rows // g)
+
+
+def ref_num_parts(rows: int, num_cus: int, group=None) -> int:
+    return max(1, (WORKGROUPS_PER_CU * num_cus) // ref_row_blocks(rows, group))
+
+
+def ref_schedule(lens, target_parts: int, rows: int, group=None) -> np.ndarray:
+    """Build the metadata array for unit lengths ``lens`` and ``target_parts``
+    parts; ``group`` overrides G(rows) (the header's row_blocks only)."""
     lens = [int(x) for x in lens]
     assert target_parts >= 1 and rows >= 1 and all(x >= 0 for x in lens)
     F = SPLIT_OVERHEAD_BLOCKS
@@ -131,7 +145,7 @@ def ref_schedule(lens, target_parts: int, rows: int) -> np.ndarray:
     off_ns = off_segs + 4 * S
     off_sl = off_ns + U + 1
     total_ints = off_sl + 2 * len(split_list)
-    row_blocks = -(-rows // ROWS_PER_WORKGROUP)
+    row_blocks = ref_row_blocks(rows, group)
     header = [num_parts, S, nslots, len(split_list), max(count) if U else 0, U,
               quota, total, target_parts, F, row_blocks, rows,
               off_segs, off_ns, off_sl, total_ints]

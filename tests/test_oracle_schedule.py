@@ -32,10 +32,10 @@ def test_hand_worked_tiny_workload():
 def test_hand_worked_no_split_and_empty_unit():
     # lens 0, 130, 64 -> blocks 0, 3, 1; total = 5 + 8 + 6 = 19; P = 2 -> quota 15.
     # part 0: unit 0 (need 5, empty segment), unit 1 (need 8), then 2 left <= F: close.
-    # part 1: unit 2.
+    # part 1: unit 2.  128 rows per unit -> one 128-row workgroup per part.
     m = ref_schedule([0, 130, 64], 2, 128)
     assert m.tolist() == [
-        2, 3, 0, 0, 1, 3, 15, 19, 2, 5, 2, 128, 19, 31, 35, 35,
+        2, 3, 0, 0, 1, 3, 15, 19, 2, 5, 1, 128, 19, 31, 35, 35,
         0, 2, 3,
         0, 0, 0, -1, 1, 0, 3, -1, 2, 0, 1, -1,
         0, 1, 2, 3,
@@ -50,12 +50,18 @@ def test_hand_worked_long_unit_even_cut():
 
 
 def test_default_part_count():
+    # G(rows) = 128 rows per workgroup above 64 rows, 64 above 32, else 32
     assert ref_num_parts(16, 256) == 256
+    assert ref_num_parts(33, 256) == 256
     assert ref_num_parts(64, 256) == 256
-    assert ref_num_parts(128, 256) == 128
-    assert ref_num_parts(256, 256) == 64
-    assert ref_num_parts(65, 256) == 128
+    assert ref_num_parts(65, 256) == 256
+    assert ref_num_parts(128, 256) == 256
+    assert ref_num_parts(129, 256) == 128
+    assert ref_num_parts(256, 256) == 128
+    assert ref_num_parts(257, 256) == 85
     assert ref_num_parts(10_000, 4) == 1
+    # an explicit group size overrides the rule
+    assert ref_num_parts(128, 256, group=64) == 128
 
 
 def check_invariants(lens, P, rows, meta):
@@ -66,7 +72,8 @@ def check_invariants(lens, P, rows, meta):
     quota = -(-total // P) + F
     assert u["num_units"] == U and u["quota"] == quota and u["total"] == total
     assert u["target_parts"] == P and u["F"] == F and u["rows"] == rows
-    assert u["row_blocks"] == -(-rows // 64)
+    group = 128 if rows > 64 else (64 if rows > 32 else 32)
+    assert u["row_blocks"] == -(-rows // group)
     segs = u["segs"]
     pp = u["part_ptr"]
     assert 0 <= u["num_parts"] <= P
