@@ -17,7 +17,7 @@ Definitions followed (citations name the page, then the section):
   ``flash_mla_with_kvcache`` call and the "Block Table Manager" paragraph).
 * Scores are scaled dot products, softmax over the visible keys, and the
   log-sum-exp is returned per query head (upstream README, "Return Values";
-  "Sparse MLA Prefill" equivalent PyTorch code for the scale placement).
+  "Sparse MLA Prefill" for the scale applied inside the scores).
 * ``s_q`` query tokens per request under MTP, with a causal mask (upstream
   README "Usage / MLA Decoding"; deepep.org example passes ``causal=True``).
 * Sparse decode: ``indices[b][i][k] = block * 64 + offset`` straight into the

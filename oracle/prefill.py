@@ -1,25 +1,31 @@
-"""Sparse MLA prefill, FP64, in the order of the pages' equivalent code.
+"""Sparse MLA prefill, FP64, written from its mathematical definition.
 
 TEST INFRASTRUCTURE ONLY -- see the package docstring.
 
-Definition (upstream FlashMLA README embedded in the DeepLink-org/
-flashmla-optimization page, "Sparse MLA Prefill", the PyTorch code the kernel
-is equivalent to): for query token i with its top-k KV rows K_i = kv[indices[i]],
+What is computed (upstream FlashMLA README embedded in the DeepLink-org/
+flashmla-optimization page, "Sparse MLA Prefill": the kernel's outputs and the
+PyTorch computation they are defined by).  For query token i and head h, let
+T_i be the multiset of valid entries of the token's top-k list and
 
-    P          = (Q_i @ K_i^T) * sm_scale * log2(e)      [h_q, topk]
-    max_logits = max over the top-k of P                  [h_q]
-    lse        = log2 sum 2^P                             [h_q]  (base 2)
-    S          = 2^(P - lse)
-    out        = S @ K_i                                  [h_q, d_v]
+    z_t = sm_scale * <q[i, h, :], kv[t, 0, :]>          t in T_i   (natural units)
+
+Then, with log2(e) converting natural units to the base-2 units the page uses,
+
+    max_logits[i, h] = log2(e) * max_t z_t
+    lse[i, h]        = log2(e) * ln sum_t exp(z_t)       (= log2 sum_t 2^(log2(e) z_t))
+    out[i, h, :]     = sum_t exp(z_t) * kv[t, 0, :d_v] / sum_t exp(z_t)
+
+i.e. softmax attention of the token's heads over its selected rows, with the
+logits' maximum and log-sum-exp reported in base 2.
 
 Readings taken where the page is silent:
 
-* Invalid entries (-1 or >= s_kv, the page's rule) are left out of every sum
-  and maximum; a query whose entries are all invalid gets out = 0 and
-  max_logits = lse = -inf.
+* An entry is invalid if it is -1 or >= s_kv (the page's rule); invalid
+  entries are left out of every sum and maximum.  A query whose entries are
+  all invalid gets out = 0 and max_logits = lse = -inf.
 * The value is the first d_v = 512 columns of a KV row, as in decode (the
-  printed ``S @ focused_kv`` is d_qk wide, the d_v = d_qk case).
-* Duplicated indices count once per occurrence.
+  page's output is d_qk wide: the d_v = d_qk case).
+* A duplicated index counts once per occurrence.
 """
 from __future__ import annotations
 
@@ -29,13 +35,26 @@ import numpy as np
 
 from .decode import _to_f64, _to_i64
 
+_LOG2E = 1.0 / math.log(2.0)
+
+
+def _attend(qi: np.ndarray, rows: np.ndarray, sm_scale: float, dv: int):
+    """Softmax attention of the heads qi [h_q, d] over rows [n, d] (n >= 1):
+    returns (out [h_q, dv], max of the logits, natural-log LSE), per head."""
+    z = sm_scale * (qi @ rows.T)                     # [h_q, n] natural-unit logits
+    zmax = np.max(z, axis=1)                         # [h_q]
+    w = np.exp(z - zmax[:, None])                    # unnormalised weights, <= 1
+    total = np.sum(w, axis=1)                        # [h_q], >= 1
+    out = (w @ rows[:, :dv]) / total[:, None]
+    return out, zmax, zmax + np.log(total)
+
 
 def ref_sparse_prefill(q, kv, indices, sm_scale: float, dv: int = 512, rows=None):
     """q [s_q, h_q, d_qk], kv [s_kv, h_kv=1, d_qk], indices [s_q, h_kv=1, topk].
 
     ``rows``: optional iterable of query tokens to compute (default: all).
     Returns (out [s_q, h_q, dv], max_logits [s_q, h_q], lse [s_q, h_q]) as
-    float64, lse in base 2; tokens not computed are NaN.
+    float64, max_logits and lse in base 2; tokens not computed are NaN.
     """
     qf = _to_f64(q)
     idx = _to_i64(indices)
@@ -46,19 +65,14 @@ def ref_sparse_prefill(q, kv, indices, sm_scale: float, dv: int = 512, rows=None
     max_logits = np.full((s_q, h_q), np.nan)
     lse = np.full((s_q, h_q), np.nan)
     for i in (range(s_q) if rows is None else rows):
-        sel = idx[i, 0]
-        sel = sel[(sel >= 0) & (sel < s_kv)]
-        if sel.size == 0:
-            out[i] = 0.0
-            max_logits[i] = -np.inf
-            lse[i] = -np.inf
+        entries = idx[i, 0]
+        valid = entries[(entries >= 0) & (entries < s_kv)]
+        if valid.size == 0:
+            out[i], max_logits[i], lse[i] = 0.0, -np.inf, -np.inf
             continue
-        focused = _to_f64(kv[sel.tolist()])[:, 0, :]               # [n, d_qk]
-        P = (qf[i] @ focused.T) * sm_scale * math.log2(math.e)    # [h_q, n]
-        mx = P.max(axis=1)
-        l2 = mx + np.log2(np.exp2(P - mx[:, None]).sum(axis=1))  # log2 sum 2^P
-        S = np.exp2(P - l2[:, None])
-        out[i] = S @ focused[:, :dv]
-        max_logits[i] = mx
-        lse[i] = l2
+        kv_rows = _to_f64(kv[valid.tolist()])[:, 0, :]   # [n, d_qk], with multiplicity
+        o, zmax, lse_e = _attend(qf[i], kv_rows, sm_scale, dv)
+        out[i] = o
+        max_logits[i] = _LOG2E * zmax
+        lse[i] = _LOG2E * lse_e
     return out, max_logits, lse
