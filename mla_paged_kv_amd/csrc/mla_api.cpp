@@ -140,7 +140,11 @@ int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool spa
   kp.row_blocks = info->row_blocks;
   kp.rows = info->rows;
   if (stages & kStageSplit) {
-    const hipError_t e = fp8 ? launch_splitkv_fp8(kp, sparse, st) : launch_decode(kp, d_qk, sparse, f16, st);
+    // units of more than 64 rows: the decode kernel (each wavefront owns 32
+    // rows and all 512 output columns, 128 rows per workgroup); otherwise, and
+    // for the FP8 cache, the pair kernel
+    const hipError_t e = (fp8 || kp.rows <= 64) ? launch_pairs(kp, d_qk, sparse, fp8, f16, st)
+                                                : launch_decode(kp, d_qk, sparse, f16, st);
     if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
   if (stages & kStageCombine)

@@ -132,15 +132,29 @@ __device__ __forceinline__ f32x16 read_acc(const f32x16& x) {
 // being computed wait for all of them, because the tile buffers are picked at
 // run time.  The kernel's own waits order them (s_waitcnt vmcnt with the
 // exact count of loads issued after, then a barrier).  They write no
-// register, so nothing of the compiler's register use can overlap them; the
-// nop covers the M0 write before an LDS DMA.
+// register, so nothing of the compiler's register use can overlap them.
+// The compiler cannot see the hazards of an instruction inside asm either, so
+// the nops are written out: a buffer resource that a VALU instruction has just
+// written (v_readlane_b32, where the compiler keeps SGPRs in VGPR lanes) needs
+// 5 wait states before a memory instruction reads it, and an M0 write needs 1
+// before an LDS DMA.
 __device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
                : "memory");
 }
 __device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
                : "memory");
+}
+// A 16-byte global load into a register tuple the compiler already holds
+// ("+v": the loaded value lands in the registers of the value it replaces,
+// so the register allocator never moves it while it is in flight).  Like the
+// direct-to-LDS loads it is invisible to the compiler's waits: the kernel
+// waits for it (s_waitcnt vmcnt(0) before the first use) and then redefines
+// the registers with an empty asm statement.
+template <typename T>
+__device__ __forceinline__ void load_b128(T& dst, const void* src) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(dst) : "v"(src) : "memory");
 }
 __device__ __forceinline__ void dma_global_b128(const void* src, uint32_t lds_addr) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
@@ -237,7 +251,6 @@ struct Tile {
   int u;     // unit
   int b1;    // end block of the segment
   int len;   // unit length (dense: cache length; sparse: topk)
-  int phys;  // dense: physical page of block pos / 2
 };
 
 }  // namespace dk
@@ -261,14 +274,14 @@ void mla_decode(SplitKVParams p) {
   constexpr int FMAX = CPR == 72 ? 8 : 16;
   constexpr int NKB = FMAX / 2;            // K-read bases (kk mod NKB)
   constexpr int NVB = FMAX / 4;            // V-read bases (ct mod NVB)
-  constexpr int IDXL = SPARSE ? 1 : 0;     // index loads per tile and wavefront
-  constexpr int ISLOT = 256;               // LDS bytes of one tile's index slot (64 lanes x 4)
-  constexpr int NISLOT = 8;                // index slots (tile k uses slot k % 8)
+  constexpr int ISLOT = 256;               // LDS bytes of one tile's slot (64 lanes x 4)
+  constexpr int NISLOT = 8;                // slots (tile k uses slot k % 8)
   static_assert(TBUF % (1024 * kWaves) == 0 && RPW * RSB == NLW * 1024, "whole loads per wavefront");
   static_assert(NCOL == 512 || NCOL == 256 || NCOL == 128, "column split");
   static_assert(kBufs * TBUF <= 160 * 1024, "tile buffers fit the LDS");
-  // the 4 tile buffers, then (sparse) the index slots
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs * TBUF + (SPARSE ? NISLOT * ISLOT : 0)];
+  // the 4 tile buffers, then the slots of the tiles' page numbers (dense) or
+  // indices (sparse)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs * TBUF + NISLOT * ISLOT];
   const uint32_t lds_base = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)lds));
 
   const int lane = threadIdx.x & 63;
@@ -285,7 +298,9 @@ void mla_decode(SplitKVParams p) {
   if (part >= p.num_parts) return;
   cint* meta = as_const(p.meta);
   // the grid covers p.num_parts parts; the device header says how many exist
-  if (part >= meta[0]) return;
+  // (header word 15 is -1 when the device scheduler rejected the lengths)
+  const bool meta_bad = meta[15] == -1;
+  if (part >= meta[0] && !meta_bad) return;
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
   cint* segs = meta + meta[12];
@@ -347,17 +362,13 @@ void mla_decode(SplitKVParams p) {
     if constexpr (SPARSE) return p.topk;
     else return as_const(p.seqlens)[u];
   };
-  auto page_of = [&](int u, int blk) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE) return 0;
-    else return as_const(p.block_table)[size_t(u) * p.bt_stride + blk];
-  };
   // first tile at or after segment s2 (segments without blocks are skipped;
   // their outputs are written when the stream passes them)
   auto first_tile_from = [&](int s2) __attribute__((always_inline)) -> Tile {
     while (s2 < seg_end && seg_b0(s2) == seg_b1(s2)) ++s2;
-    if (s2 >= seg_end) return Tile{seg_end, 0, 0, 0, 1, 0};
+    if (s2 >= seg_end) return Tile{seg_end, 0, 0, 0, 1};
     const int u = seg_u(s2), b0 = seg_b0(s2);
-    return Tile{s2, 2 * b0, u, seg_b1(s2), unit_len(u), page_of(u, b0)};
+    return Tile{s2, 2 * b0, u, seg_b1(s2), unit_len(u)};
   };
   // a block's second half exists unless the unit ends in its first half
   auto has_next_half = [&](const Tile& t) __attribute__((always_inline)) -> bool {
@@ -368,36 +379,45 @@ void mla_decode(SplitKVParams p) {
   };
   auto next_tile = [&](const Tile& t) __attribute__((always_inline)) -> Tile {
     if (t.s >= seg_end) return t;
-    if (has_next_half(t)) return Tile{t.s, t.pos + 1, t.u, t.b1, t.len, t.phys};
+    if (has_next_half(t)) return Tile{t.s, t.pos + 1, t.u, t.b1, t.len};
     const int nb = (t.pos >> 1) + 1;
-    if (nb < t.b1) return Tile{t.s, 2 * nb, t.u, t.b1, t.len, page_of(t.u, nb)};
+    if (nb < t.b1) return Tile{t.s, 2 * nb, t.u, t.b1, t.len};
     return first_tile_from(t.s + 1);
   };
 
-  // ---- sparse index loads ----
-  // The 32 indices of a tile are copied into LDS slot (tile number % 8) by
-  // one direct-to-LDS load per wavefront (lanes 32..63 repeat lanes 0..31).
-  // Positions past the list read its last entry and are invalid by
-  // position.  Every wavefront issues the load, so each step costs exactly
-  // one vector-memory operation per wavefront for the indices.
-  auto idx_rsrc = [&]() __attribute__((always_inline)) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p.indices), 0, 0x7FFFFFFF,
-                                            kBufferWord3);
+  // ---- per-tile metadata through LDS ----
+  // What a tile's gather needs -- its physical page (dense) or its 32 row
+  // indices (sparse) -- is copied into LDS slot (tile number % 8) by one
+  // direct-to-LDS load per wavefront three steps ahead of the gather, and read
+  // back after the step's barrier.  (A scalar load instead would be waited
+  // for wherever the compiler first moves its register.)  Dense: every lane
+  // loads the same block-table entry.  Sparse: lanes 0..31 load the tile's
+  // 32 indices, lanes 32..63 repeat them; positions past the list read its
+  // last entry and are invalid by position.  Every wavefront issues the load,
+  // so each step costs exactly one more vector-memory operation per wavefront.
+  auto meta_rsrc = [&]() __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(SPARSE ? p.indices : p.block_table), 0, 0x7FFFFFFF, kBufferWord3);
   };
-  auto load_idx = [&](const Tile& t, int slot) __attribute__((always_inline)) {
+  auto load_slot = [&](const Tile& t, int slot) __attribute__((always_inline)) {
+    uint32_t off;
     if constexpr (SPARSE) {
       int pos = t.pos * kTile + lrow;
       pos = pos < t.len ? pos : t.len - 1;
-      const uint32_t off = uint32_t((size_t(t.u) * p.topk + pos) * 4);
-      dma_b32(idx_rsrc(), off, lds_base + kBufs * TBUF + slot * ISLOT);
+      off = uint32_t((size_t(t.u) * p.topk + pos) * 4);
+    } else {
+      off = uint32_t((size_t(t.u) * p.bt_stride + (t.pos >> 1)) * 4);
     }
+    dma_b32(meta_rsrc(), off, lds_base + kBufs * TBUF + slot * ISLOT);
   };
-  // this lane's index of a tile (lanes 0..31: tile token = lane), read from
-  // its slot once the load has landed; -1 past the list
-  auto read_idx = [&](const Tile& t, int slot) __attribute__((always_inline)) -> int {
-    if constexpr (!SPARSE) return 0;
+  // this lane's index of a sparse tile (lanes 0..31: tile token = lane), -1
+  // past the list; or the dense tile's page (uniform)
+  auto read_slot = [&](const Tile& t, int slot) __attribute__((always_inline)) -> int {
     const int v = *reinterpret_cast<const int*>(lds + kBufs * TBUF + slot * ISLOT + 4 * lrow);
-    return t.pos * kTile + lrow < t.len ? v : -1;
+    if constexpr (SPARSE)
+      return t.pos * kTile + lrow < t.len ? v : -1;
+    else
+      return __builtin_amdgcn_readfirstlane(v);
   };
 
   // ---- tile gathers ----
@@ -417,8 +437,9 @@ void mla_decode(SplitKVParams p) {
     int idx;   // sparse: this lane's row index (lanes 0..31; substituted)
     uint32_t vmask;  // sparse: valid tokens of the tile (bit t)
   };
-  auto plan_tile = [&](const Tile& t, int idx) __attribute__((always_inline)) -> Plan {
-    Plan g{t.phys, (t.pos & 1) * kTile, kTile - 1, 0, 0xFFFFFFFFu};
+  auto plan_tile = [&](const Tile& t, int sv) __attribute__((always_inline)) -> Plan {
+    Plan g{SPARSE ? 0 : sv, (t.pos & 1) * kTile, kTile - 1, 0, 0xFFFFFFFFu};
+    const int idx = sv;
     if constexpr (SPARSE) {
       const bool ok = idx >= 0 && idx < p.num_rows;
       g.vmask = uint32_t(__ballot(ok && lane < 32));
@@ -475,7 +496,7 @@ void mla_decode(SplitKVParams p) {
   };
 
   // ---- per-segment state ----
-  bf16x8 qf[KK];           // Q^T fragments of the wavefront's 32 rows
+  bf16x8 qf[KK] = {};      // Q^T fragments of the wavefront's 32 rows
   f32x16 acc[NCT];         // O^T accumulator (AGPRs)
   float m_run = -__builtin_inff();    // reference maximum (base 2, scaled) of the lane's row
   float m_exact = -__builtin_inff();  // exact row maximum of the scaled logits (base 2)
@@ -498,11 +519,26 @@ void mla_decode(SplitKVParams p) {
     m_exact = -__builtin_inff();
     l_run = 0.f;
   };
-  // rows past the unit's last row read that last row (never written back)
+  // rows past the unit's last row read that last row (never written back);
+  // the loads are waited for at the start of the segment's first step
+  // (WIDE kernels spill registers, and a spill could copy the registers of a
+  // load still in flight, so their loads are the compiler's own; they wait
+  // for everything at every step anyway.)
   auto load_q = [&](int u) __attribute__((always_inline)) {
     const uint16_t* qp = p.q + row_index(u, row_ok ? row : p.rows - 1) * D_QK + 8 * lgrp;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+    for (int kk = 0; kk < KK; ++kk) {
+      if constexpr (WIDE)
+        qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+      else
+        load_b128(qf[kk], qp + kk * 16);
+    }
+  };
+  // after a wait that covers the query loads: from here on the compiler may
+  // treat the registers as holding their values
+  auto q_landed = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[kk]));
   };
 
   // Writes the segment result of this lane's row (its NCOL columns): 16-bit O
@@ -736,6 +772,24 @@ void mla_decode(SplitKVParams p) {
     for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);
   };
 
+  // ---- lengths the device scheduler rejected ----
+  // Every output row of the call gets O = 0 and LSE = NaN (and max_logits =
+  // NaN), rather than whatever the buffers held: workgroup (part, row block)
+  // takes units part, part + grid parts, ...
+  if (meta_bad) {
+    if (!row_ok) return;
+    for (int u = part; u < meta[5]; u += p.num_parts) {
+      const size_t orow = row_index(u, row);
+      uint16_t* o = p.out + orow * kDV + NCOL * cq + 4 * lgrp;
+      for (int c = 0; c < NCOL; c += 8) *reinterpret_cast<uint2*>(o + c) = uint2{0, 0};
+      if (lgrp == 0 && cq == 0) {
+        p.lse[orow] = __builtin_nanf("");
+        if (p.max_logits) p.max_logits[orow] = __builtin_nanf("");
+      }
+    }
+    return;
+  }
+
   // ---- the stream of the part ----
   // leading segments without tiles
   int cs0 = seg_begin;
@@ -746,18 +800,17 @@ void mla_decode(SplitKVParams p) {
   if (cs0 >= seg_end) return;
 
   // Tiles t .. t+5 are tracked: t is computed, t+1 and t+2 are in flight or
-  // landed, t+3 is gathered during step t (its plan needs its page, or for
-  // sparse its indices, loaded three steps earlier), t+4 and t+5 are looked
-  // up ahead, and the end of step t looks up t+6 (and loads its indices).
+  // landed, t+3 is gathered during step t (its plan needs its slot, loaded
+  // three steps earlier), t+4 and t+5 are looked up ahead, and the end of
+  // step t looks up t+6 and loads its slot.
   // All metadata lookups of a step come after its compute: a scalar load in
   // flight shares the LDS wait counter and would make every operand wait of
   // the tile a full drain.  Past the end of the stream a tile repeats the
   // last real one, so its (unused) loads are in bounds and every step issues
   // the same number of vector-memory operations, which the waits count on:
-  //   dense  step t: NLW gather loads of tile t+3;
-  //   sparse step t: NLW gather loads of tile t+3, then the index load of t+6.
+  //   step t: NLW gather loads of tile t+3, then the slot load of tile t+6.
   auto clamp_end = [&](const Tile& n, const Tile& prev) __attribute__((always_inline)) -> Tile {
-    return n.s < seg_end ? n : Tile{seg_end, prev.pos, prev.u, prev.b1, prev.len, prev.phys};
+    return n.s < seg_end ? n : Tile{seg_end, prev.pos, prev.u, prev.b1, prev.len};
   };
   Tile t0 = first_tile_from(cs0);
   load_q(t0.u);
@@ -770,34 +823,32 @@ void mla_decode(SplitKVParams p) {
   Tile t5 = clamp_end(next_tile(t4), t4);
   uint32_t vm0, vm1, vm2;
   {
-    // sparse: the indices of tiles 0..2 are needed now; those of 3..5 follow
-    // the gathers of 0..2 in the steady-state order
-    load_idx(t0, 0);
-    load_idx(t1, 1);
-    load_idx(t2, 2);
-    if constexpr (SPARSE) {
-      wait_vmem_n<0>();
-      lds_barrier();
-    }
+    // the slots of tiles 0..2 are needed now; those of 3..5 follow the
+    // gathers of 0..2 in the steady-state order
+    load_slot(t0, 0);
+    load_slot(t1, 1);
+    load_slot(t2, 2);
+    wait_vmem_n<0>();
+    lds_barrier();
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const Plan g0 = plan_tile(t0, read_idx(t0, 0));
+    const Plan g0 = plan_tile(t0, read_slot(t0, 0));
     vm0 = g0.vmask;
 #pragma unroll
     for (int i = 0; i < NLW; ++i) gather_one(g0, 0 * TBUF, i, ln);
-    load_idx(t3, 3);
-    const Plan g1 = plan_tile(t1, read_idx(t1, 1));
+    load_slot(t3, 3);
+    const Plan g1 = plan_tile(t1, read_slot(t1, 1));
     vm1 = g1.vmask;
 #pragma unroll
     for (int i = 0; i < NLW; ++i) gather_one(g1, 1 * TBUF, i, ln);
-    load_idx(t4, 4);
-    const Plan g2 = plan_tile(t2, read_idx(t2, 2));
+    load_slot(t4, 4);
+    const Plan g2 = plan_tile(t2, read_slot(t2, 2));
     vm2 = g2.vmask;
 #pragma unroll
     for (int i = 0; i < NLW; ++i) gather_one(g2, 2 * TBUF, i, ln);
-    load_idx(t5, 5);
+    load_slot(t5, 5);
   }
-  // outstanding now (oldest first): q, g0, [ix3], g1, [ix4], g2, [ix5]
+  // outstanding now (oldest first): q, g0, s3, g1, s4, g2, s5
   bool seg_start = false;  // first step of a segment after the first one
   int tnum = 0;            // stream position of t0 (buffer tnum % 4, index slot tnum % 8)
 
@@ -816,10 +867,11 @@ void mla_decode(SplitKVParams p) {
     if (seg_start || WIDE)
       wait_vmem_n<0>();
     else
-      wait_vmem_n<2 * NLW + 2 * IDXL>();
+      wait_vmem_n<2 * NLW + 2>();
+    q_landed();
     lds_barrier();
     const bool has_next = t1.s < seg_end;
-    const Plan g3 = plan_tile(t3, read_idx(t3, (tnum + 3) % NISLOT));
+    const Plan g3 = plan_tile(t3, read_slot(t3, (tnum + 3) % NISLOT));
     const uint32_t vm3 = g3.vmask;
     const bool last = is_last(t0);
     const int next_q_unit = (last && has_next) ? t1.u : -1;
@@ -848,7 +900,7 @@ void mla_decode(SplitKVParams p) {
     }
     seg_start = last && has_next;
     const Tile t6 = clamp_end(next_tile(t5), t5);
-    load_idx(t6, (tnum + 6) % NISLOT);
+    load_slot(t6, (tnum + 6) % NISLOT);
     if (!has_next) break;
     t0 = t1;
     t1 = t2;
@@ -888,9 +940,11 @@ hipError_t launch_decode_d(const SplitKVParams& p, bool sparse, hipStream_t stre
     else if (!wide) go(mla_decode<D_QK, true, false, F16, NC>);
     else go(mla_decode<D_QK, true, true, F16, NC>);
   };
-  if (rbk == 128) cases(std::integral_constant<int, 512>{});
-  else if (rbk == 64) cases(std::integral_constant<int, 256>{});
-  else cases(std::integral_constant<int, 128>{});
+  // (units of more than 64 rows only: 128 rows per workgroup, each wavefront
+  // holding all 512 output columns of its rows; the column splits of the
+  // template are not instantiated)
+  if (rbk != 128) return hipErrorInvalidValue;
+  cases(std::integral_constant<int, 512>{});
   return hipGetLastError();
 }
 

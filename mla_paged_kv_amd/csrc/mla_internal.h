@@ -14,10 +14,10 @@ constexpr int32_t kHeaderInts = 16;
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-// Query rows per workgroup for units of `rows` query rows: 128 when rows >
-// 64, 64 when rows > 32, else 32 (the decode kernel's column split follows
-// it).  A part spans ceil(rows / rows_per_group(rows)) workgroups.
-inline int32_t rows_per_group(int32_t rows) { return rows > 64 ? 128 : (rows > 32 ? 64 : 32); }
+// Query rows per workgroup for units of `rows` query rows: 128 when rows > 64
+// (the decode kernel), else 64 (the pair kernel).  A part spans
+// ceil(rows / rows_per_group(rows)) workgroups.
+inline int32_t rows_per_group(int32_t rows) { return rows > 64 ? 128 : 64; }
 
 int32_t default_num_parts(int32_t rows, int32_t num_cus);
 size_t metadata_capacity(int32_t num_units, int32_t target_parts);

@@ -58,8 +58,12 @@ struct CombineParams {
 template <int D_QK, bool F16>
 hipError_t launch_decode_d(const SplitKVParams& p, bool sparse, hipStream_t stream);
 hipError_t launch_decode(const SplitKVParams& p, int d_qk, bool sparse, bool f16, hipStream_t stream);
-// FP8-with-scale caches (mla_splitkv_kernel.h; 64 query rows per workgroup)
-hipError_t launch_splitkv_fp8(const SplitKVParams& p, bool sparse, hipStream_t stream);
+// The pair kernel (mla_splitkv_kernel.h; wavefront pairs share 32 query rows,
+// 64 rows per workgroup): FP8-with-scale caches, and bf16 / fp16 caches for
+// units of at most 64 query rows.
+hipError_t launch_pairs(const SplitKVParams& p, int d_qk, bool sparse, bool fp8, bool f16,
+                        hipStream_t stream);
+hipError_t launch_pairs_f16(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -193,7 +193,10 @@ __global__ __launch_bounds__(kThreads) void mla_sched_dev(SchedDevParams p) {
   }
   __syncthreads();
   if (s_bad) {  // a length out of range: an empty schedule that runs nothing
-    if (t < kMetaHeaderInts) meta[t] = t == kMetaHeaderInts - 1 ? -1 : 0;
+    // (the unit and row counts stay, so the decode kernels can mark every
+    // output row of the call as invalid)
+    if (t < kMetaHeaderInts)
+      meta[t] = t == kMetaHeaderInts - 1 ? -1 : (t == 5 ? U : (t == 11 ? p.rows : 0));
     return;
   }
   const int NP = s_np;

@@ -257,8 +257,10 @@ void mla_splitkv(SplitKVParams p) {
 
   cint* meta = as_const(p.meta);
   // the grid covers p.num_parts parts, the device header says how many exist
-  // (fewer only when the metadata was built on the device)
-  if (part >= meta[0]) return;
+  // (fewer only when the metadata was built on the device; header word 15 is
+  // -1 when the device scheduler rejected the lengths)
+  const bool meta_bad = meta[15] == -1;
+  if (part >= meta[0] && !meta_bad) return;
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
   cint* segs = meta + meta[12];
@@ -397,7 +399,8 @@ void mla_splitkv(SplitKVParams p) {
         const uint8_t* src = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * RSB + in_row;
         __builtin_amdgcn_global_load_lds(src, to, 16, 0, 0);
       } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), to, 16, r * RSB + in_row, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), to, 16,
+                                                 uint32_t(r) * uint32_t(RSB) + uint32_t(in_row), 0, 0, 0);
       }
     } else {
       // in-page offset of source chunk q ^ f(t), moved down to row tmax for
@@ -458,7 +461,8 @@ void mla_splitkv(SplitKVParams p) {
             const uint8_t* src = reinterpret_cast<const uint8_t*>(p.kv) + size_t(r) * SROW + cb;
             __builtin_amdgcn_global_load_lds(src, to, 16, 0, 0);
           } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), to, 16, r * SROW + cb, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc(), to, 16,
+                                                     uint32_t(r) * uint32_t(SROW) + uint32_t(cb), 0, 0, 0);
           }
         } else {
           if (t > g.tmax) t = g.tmax;
@@ -828,9 +832,8 @@ void mla_splitkv(SplitKVParams p) {
     int s, blk, u;
     bool last;
   };
-  int la_s = seg_begin, la_u = 0, la_b1 = 0;  // cached segment
+  int la_u = 0, la_b1 = 0;  // cached segment
   auto load_seg = [&](int s2) __attribute__((always_inline)) {
-    la_s = s2;
     la_u = seg_u(s2);
     la_b1 = seg_b1(s2);
   };
@@ -848,6 +851,24 @@ void mla_splitkv(SplitKVParams p) {
     if (!t.last) return Tile{t.s, t.blk + 1, t.u, t.blk + 2 >= la_b1};
     return first_tile_from(t.s + 1);
   };
+
+  // Lengths the device scheduler rejected: every output row of the call gets
+  // O = 0 and LSE = NaN (and max_logits = NaN), rather than whatever the
+  // buffers held; workgroup (part, row block) takes units part, part + grid
+  // parts, ...
+  if (meta_bad) {
+    if (!row_ok) return;
+    for (int u = part; u < meta[5]; u += p.num_parts) {
+      const size_t orow = row_index(u, row);
+      uint16_t* o = p.out + orow * kDV + 256 * half + 4 * lgrp;
+      for (int c = 0; c < 256; c += 8) *reinterpret_cast<uint2*>(o + c) = uint2{0, 0};
+      if (lgrp == 0 && half == 0) {
+        p.lse[orow] = __builtin_nanf("");
+        if (p.max_logits) p.max_logits[orow] = __builtin_nanf("");
+      }
+    }
+    return;
+  }
 
   // leading segments without tiles
   int cs0 = seg_begin;
@@ -992,10 +1013,12 @@ void mla_splitkv(SplitKVParams p) {
 #endif
 }
 
-// Launches the FP8-cache kernel (64 query rows per workgroup, whatever the
-// rows per workgroup the schedule was sized for: a part then spans
-// ceil(rows / 64) workgroups).
-inline hipError_t launch_splitkv_fp8_t(const SplitKVParams& p, bool sparse, hipStream_t stream) {
+// Launches the pair kernel (64 query rows per workgroup, whatever the rows per
+// workgroup the schedule was sized for: a part then spans ceil(rows / 64)
+// workgroups) for one element type: the FP8-with-scale cache (bf16 only) or
+// bf16 / fp16 caches of 576- or 512-wide rows.
+template <bool F16>
+hipError_t launch_pairs_t(const SplitKVParams& p, int d_qk, bool sparse, bool fp8, hipStream_t stream) {
   const int row_blocks = (p.rows + kRowsPerGroup - 1) / kRowsPerGroup;
   const int groups = p.num_parts * row_blocks;
   if (groups <= 0) return hipSuccess;
@@ -1004,11 +1027,34 @@ inline hipError_t launch_splitkv_fp8_t(const SplitKVParams& p, bool sparse, hipS
   const dim3 grid(groups), block(256);
   // Sparse rows are addressed with 32-bit byte offsets while the pool (plus
   // the past-the-end row an all-invalid tile reads) fits in 32 bits.
-  const bool wide = (uint64_t(p.num_rows) + 2) * uint64_t(kFp8RowBytes) > 0xFFFFFFFFull;
+  const uint64_t row_bytes = fp8 ? kFp8RowBytes : uint64_t(d_qk) * 2;
+  const bool wide = (uint64_t(p.num_rows) + 2) * row_bytes > 0xFFFFFFFFull;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, q); };
-  if (!sparse) go(mla_splitkv<576, false, false, true, false>);
-  else if (!wide) go(mla_splitkv<576, true, false, true, false>);
-  else go(mla_splitkv<576, true, true, true, false>);
+  if constexpr (F16) {
+    if (d_qk == 576) {
+      if (!sparse) go(mla_splitkv<576, false, false, false, true>);
+      else if (!wide) go(mla_splitkv<576, true, false, false, true>);
+      else go(mla_splitkv<576, true, true, false, true>);
+    } else {
+      if (!sparse) go(mla_splitkv<512, false, false, false, true>);
+      else if (!wide) go(mla_splitkv<512, true, false, false, true>);
+      else go(mla_splitkv<512, true, true, false, true>);
+    }
+  } else {
+    if (fp8) {
+      if (!sparse) go(mla_splitkv<576, false, false, true, false>);
+      else if (!wide) go(mla_splitkv<576, true, false, true, false>);
+      else go(mla_splitkv<576, true, true, true, false>);
+    } else if (d_qk == 576) {
+      if (!sparse) go(mla_splitkv<576, false, false, false, false>);
+      else if (!wide) go(mla_splitkv<576, true, false, false, false>);
+      else go(mla_splitkv<576, true, true, false, false>);
+    } else {
+      if (!sparse) go(mla_splitkv<512, false, false, false, false>);
+      else if (!wide) go(mla_splitkv<512, true, false, false, false>);
+      else go(mla_splitkv<512, true, true, false, false>);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -42,8 +42,8 @@ consecutive workspace slots, numbered over split units in unit order; an unsplit
 unit's single segment gets slot -1 (written straight to the output).
 
 Default part count: ``rows`` query rows per unit are processed ``G(rows)``
-per workgroup, where G(rows) = 128 if rows > 64, 64 if 32 < rows <= 64, else
-32, and one workgroup is resident per compute unit (a workgroup's tile buffers
+per workgroup, where G(rows) = 128 if rows > 64, else 64, and one workgroup is
+resident per compute unit (a workgroup's tile buffers
 fill most of the LDS), so that every part starts at once:
 ``row_blocks = ceil(rows / G(rows))`` and ``P = max(1, num_cus // row_blocks)``.
 G is a parameter of the specification (``rows_per_group``), not a property the
@@ -72,9 +72,7 @@ HEADER_INTS = 16
 
 def rows_per_group(rows: int) -> int:
     """G(rows): query rows per workgroup (see the specification above)."""
-    if rows > 64:
-        return 128
-    return 64 if rows > 32 else 32
+    return 128 if rows > 64 else 64
 
 
 def ref_row_blocks(rows: int, group=None) -> int:

@@ -2,8 +2,15 @@
 binding, run the FP64 oracle on the same seeded inputs, compare.
 
 Tolerances: relative L2 error of O <= 1e-2 (checked over every compared
-element and, more strictly, per query row) and absolute LSE error <= 1e-3;
-a row that sees no key must give O == 0 exactly and LSE == -inf on both sides.
+element and, more strictly, per query row), every element of O within 5e-2 of
+its row's RMS, and absolute LSE error <= 1e-3; a row that sees no key must give
+O == 0 exactly and LSE == -inf on both sides.
+
+The element bound: rounding O to bf16 moves an element by at most 2^-9 of
+itself (about 0.002 of the row RMS for elements up to 4 RMS), and rounding the
+softmax weights to bf16 adds errors of the same relative size that average
+over the keys, so 5e-2 leaves more than tenfold headroom while a wrong column
+of a few percent fails it.
 """
 import sys
 
@@ -14,6 +21,7 @@ import mla_paged_kv_amd as mla
 import oracle
 
 O_REL_L2 = 1e-2
+O_ELEM_RMS = 5e-2
 LSE_ABS = 1e-3
 
 
@@ -86,9 +94,14 @@ def compare(O, LSE, O_ref, LSE_ref, what=""):
     row_den = np.linalg.norm(r[fin], axis=1)
     row_rel = np.linalg.norm(o[fin] - r[fin], axis=1) / np.maximum(row_den, 1e-30)
     worst = float(row_rel.max()) if fin.any() else 0.0
+    # every element within O_ELEM_RMS of its row's RMS: a few wrong columns
+    # cannot hide under a 512-wide row's L2 norm
+    row_rms = np.sqrt(np.mean(r[fin] ** 2, axis=1))
+    elem = float(np.max(np.abs(o[fin] - r[fin]) / np.maximum(row_rms, 1e-30)[:, None])) if fin.any() else 0.0
     log(f"  {what}: rows={int(sel.sum())} rel_l2={rel:.3e} worst_row_rel_l2={worst:.3e} "
-        f"max_lse_err={lerr:.3e}")
+        f"max_elem/row_rms={elem:.3e} max_lse_err={lerr:.3e}")
     assert rel <= O_REL_L2, f"{what}: rel L2 {rel}"
     assert worst <= O_REL_L2, f"{what}: worst row rel L2 {worst}"
+    assert elem <= O_ELEM_RMS, f"{what}: an element is {elem} of its row's RMS off"
     assert lerr <= LSE_ABS, f"{what}: LSE err {lerr}"
     return rel, worst, lerr

@@ -102,6 +102,25 @@ def test_device_metadata_negative_length_gives_empty_schedule():
     m = mla.mla_get_metadata_device(sl, 1, 16, num_parts=4)
     hdr = m.meta_dev[:16].cpu().numpy()
     assert hdr[0] == 0 and hdr[3] == 0 and hdr[15] == -1
+    assert hdr[5] == 3 and hdr[11] == 16  # units and rows stay for the decode kernels
+
+
+@pytest.mark.parametrize("h_q", [16, 128])  # pair kernel (<= 64 rows), decode kernel (> 64 rows)
+def test_device_metadata_negative_length_marks_every_output(h_q):
+    """A decode with a schedule the device scheduler rejected writes O = 0 and
+    LSE = NaN for every row, not what the buffers held before."""
+    case = make_dense_case(503, B=3, s_q=1, h_q=h_q, seqlens=[100, 5, 50])
+    d = to_device(case)
+    sl = torch.as_tensor(np.array([100, -1, 50], np.int32)).cuda()
+    m = mla.mla_get_metadata_device(sl, 1, h_q, num_parts=4)
+    log(f"rejected device metadata, h_q={h_q}")
+    out = torch.full((3, 1, h_q, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((3, 1, h_q), 7.0, dtype=torch.float32, device="cuda")
+    mla.mla_decode_paged(d["q"], d["kvcache"], d["block_table"], d["cache_seqlens"], 512, m,
+                         softmax_scale=case["softmax_scale"], out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out == 0).all()), "every output element is 0"
+    assert bool(torch.isnan(lse).all()), "every LSE is NaN"
 
 
 def test_device_metadata_reuses_buffer_across_calls():

@@ -146,8 +146,8 @@ def test_fp8_sparse_topk2048_full_size():
     _check(case, num_parts=0, batches=list(range(0, 32, 5)), what="fp8 sparse topk 2048")
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_sparse_pool_past_4gib(fp8):
+@pytest.mark.parametrize("fp8,h_q", [(False, 16), (True, 16), (False, 128)])
+def test_sparse_pool_past_4gib(fp8, h_q):
     """Rows beyond byte offset 2^32 of the pool: the 64-bit addressing path."""
     row_bytes = 656 if fp8 else 1152
     d_qk = 576
@@ -159,7 +159,7 @@ def test_sparse_pool_past_4gib(fp8):
     pos[0, :5] = -1
     used = np.unique(pos[pos >= 0])
     # small case with the same selected rows, then placed into the big pool
-    src = make_sparse_case(817, B=1, s_q=1, h_q=16, active_h_q=16, topk=64,
+    src = make_sparse_case(817, B=1, s_q=1, h_q=h_q, active_h_q=h_q, topk=64,
                            cache_len=len(used) + 64, invalid_tail=0, d_qk=d_qk, kv_fp8=fp8)
     rows_small = src["kvcache"].reshape(-1, src["kvcache"].shape[-1])[:len(used)]
     log(f"pool of {n_rows} rows ({n_rows * row_bytes / 2**30:.2f} GiB), fp8={fp8}")
@@ -167,14 +167,14 @@ def test_sparse_pool_past_4gib(fp8):
     kv_cpu = torch.zeros(shape, dtype=torch.uint8 if fp8 else torch.bfloat16)
     flat = kv_cpu.view(-1, shape[-1])
     flat[torch.from_numpy(used)] = rows_small
-    q = src["q"][:1].expand(B, 1, 16, d_qk).contiguous()
+    q = src["q"][:1].expand(B, 1, h_q, d_qk).contiguous()
     idx = torch.from_numpy(pos.reshape(B, 1, topk).astype(np.int32))
-    case = dict(src, q=q, kvcache=kv_cpu, indices=idx, topk=topk, active_h_q=16,
+    case = dict(src, q=q, kvcache=kv_cpu, indices=idx, topk=topk, active_h_q=h_q,
                 cache_seqlens=torch.full((B,), n_rows, dtype=torch.int32))
     d = dict(case, q=q.cuda(), kvcache=kv_cpu.cuda(), indices=idx.cuda())
     meta = metadata(case, num_parts=0)
     out, lse = run_gpu(d, meta)
     O, LSE = to_np(out, lse)
-    compare(O, LSE, *run_oracle(case), f"pool past 4 GiB fp8={fp8}")
+    compare(O, LSE, *run_oracle(case), f"pool past 4 GiB fp8={fp8} h_q={h_q}")
     del d
     torch.cuda.empty_cache()

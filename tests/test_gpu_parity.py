@@ -2,8 +2,9 @@
 
 Small cases are compared on every output; the five named workloads run at full
 size in the launch configuration the benchmark uses (default part count),
-compared on every request the oracle can finish quickly (all of them except
-the MTP workload, which is sampled).  Edge cases: empty and one-token caches,
+compared on every request.  Units of more than 64 query rows run on the decode
+kernel (128 rows per workgroup), smaller ones on the pair kernel; both are
+covered, dense and sparse.  Edge cases: empty and one-token caches,
 exact page multiples, causal rows that see nothing, NaN-poisoned tails and
 spare blocks, invalid and duplicate sparse indices, forced split counts from 1
 to past 64 per request, run-to-run and block-permutation bit identity, and
@@ -69,7 +70,8 @@ def test_empty_and_fully_masked_rows():
 
 @pytest.mark.parametrize("s_q,active,h_q,d_qk,topk,invalid", [
     (1, 16, 64, 512, 2048, 102), (2, 16, 64, 512, 300, 7), (1, 64, 64, 512, 130, 0),
-    (1, 8, 16, 576, 200, 13), (3, 16, 32, 576, 64, 64),
+    (1, 8, 16, 576, 200, 13), (3, 16, 32, 576, 64, 64), (1, 128, 128, 576, 300, 7),
+    (2, 96, 128, 512, 520, 33),
 ])
 def test_sparse_small(s_q, active, h_q, d_qk, topk, invalid):
     case = make_sparse_case(13, B=3, s_q=s_q, h_q=h_q, active_h_q=active, topk=topk,
@@ -212,10 +214,9 @@ def test_stages_compose_to_decode():
 def test_named_workload_full_size(k):
     case = make_config(k)
     log(f"workload {k}: {case['name']}")
-    batches = None
-    if k == 3:
-        batches = list(range(0, 128, 9))  # 15 of 128 requests (each 2 x 128 rows x 4096 keys)
-    _check(case, num_parts=0, batches=batches, what=f"workload {k}")
+    # every request of every workload is checked (workload 3: all 128
+    # requests, so every workgroup column of its schedule)
+    _check(case, num_parts=0, what=f"workload {k}")
 
 
 @pytest.mark.parametrize("fp8", [False, True])

@@ -50,7 +50,7 @@ def test_hand_worked_long_unit_even_cut():
 
 
 def test_default_part_count():
-    # G(rows) = 128 rows per workgroup above 64 rows, 64 above 32, else 32
+    # G(rows) = 128 rows per workgroup above 64 rows, else 64
     assert ref_num_parts(16, 256) == 256
     assert ref_num_parts(33, 256) == 256
     assert ref_num_parts(64, 256) == 256
@@ -72,7 +72,7 @@ def check_invariants(lens, P, rows, meta):
     quota = -(-total // P) + F
     assert u["num_units"] == U and u["quota"] == quota and u["total"] == total
     assert u["target_parts"] == P and u["F"] == F and u["rows"] == rows
-    group = 128 if rows > 64 else (64 if rows > 32 else 32)
+    group = 128 if rows > 64 else 64
     assert u["row_blocks"] == -(-rows // group)
     segs = u["segs"]
     pp = u["part_ptr"]
