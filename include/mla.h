@@ -28,7 +28,8 @@
  *  - Pointers marked "device" are device memory owned by the caller; "host" is
  *    host memory owned by the caller.  The library keeps no pointer after it
  *    returns, allocates nothing, and holds no global state other than a
- *    thread-local message for the last error.
+ *    thread-local message for the last error and the static device array of
+ *    mla_decode_paged_noalloc (one per GPU, with its address).
  *  - Tensors are dense and row-major (C-contiguous) in the layout stated.
  *  - Decode calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  They neither synchronise nor allocate.
@@ -74,7 +75,7 @@ typedef struct mla_sched_info {
   int32_t total_cost;      /* sum over units of blocks + per-segment overhead */
   int32_t target_parts;    /* part count the schedule was built for */
   int32_t overhead;        /* per-segment overhead in blocks (5) */
-  int32_t row_blocks;      /* workgroups per part: ceil(rows / 64) */
+  int32_t row_blocks;      /* workgroups per part: ceil(rows / G), G = 128 if rows > 64 else 64 */
   int32_t rows;            /* query rows per unit: dense s_q*heads, sparse heads */
   int32_t off_segs;        /* int offset of segs[num_segments][4] = (u, blk0, blk1, slot) */
   int32_t off_num_splits;  /* int offset of num_splits[num_units + 1] (cumulative) */
@@ -268,6 +269,34 @@ int mla_splitkv_sparse(const void* q, const void* kvcache, const int32_t* indice
 int mla_combine(const int32_t* meta_dev, const mla_sched_info* info, int32_t batch, int32_t s_q,
                 int32_t h_q, int32_t dv, int32_t sparse, const void* workspace,
                 size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * mla_decode_paged_noalloc -- mla_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks and results as
+ * mla_decode_paged (bf16), without workspace/workspace_bytes: the fp32 split
+ * partials go to a static device array of MLA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine); the first
+ * call on a device looks up that device's array address.
+ *
+ *   Limit: mla_workspace_bytes(info, dv) must be <= MLA_NOALLOC_SCRATCH_BYTES
+ *   (128 MiB: every bundled schedule of up to 256 rows per unit and 256
+ *   parts fits), else MLA_E_NOSPC and nothing is enqueued.
+ *   Sharing: every call on one GPU uses the same array.  Calls that overlap
+ *   on one GPU (different streams, or host threads, with no ordering between
+ *   them) race on it; calls ordered on one stream do not.  Nothing in it needs
+ *   to start at zero: each call writes every partial its combine reads.
+ *   Errors: those of mla_decode_paged, MLA_E_NOSPC as above, MLA_E_HIP if the
+ *   device or the array's address cannot be queried.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int mla_decode_paged_noalloc(const void* q, const void* kvcache, const int32_t* block_table,
+                             const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                             int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t dv,
+                             int32_t num_blocks, int32_t page_block_size, int32_t bt_stride,
+                             int32_t causal, float softmax_scale, const int32_t* meta_dev,
+                             const mla_sched_info* info, void* out, float* lse, void* stream);
 
 /*
  * mla_sparse_prefill -- sparse MLA prefill (the pages' flash_mla_sparse_fwd:

@@ -12,6 +12,7 @@ Entry points mirror the C ABI names:
 * ``mla_get_metadata``   -- tile scheduler (host), once per decode step
 * ``mla_get_metadata_device`` -- the same scheduler as a GPU kernel (no sync)
 * ``mla_decode_paged``   -- dense paged decode, once per layer
+* ``mla_decode_paged_noalloc`` -- the same without a workspace (static scratch)
 * ``mla_decode_sparse``  -- top-k sparse decode, once per layer
 * ``mla_sparse_prefill`` -- top-k sparse prefill (out, max_logits, base-2 lse)
 
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     mla_combine,
     mla_decode_paged,
+    mla_decode_paged_noalloc,
     mla_decode_sparse,
     mla_get_metadata,
     mla_get_metadata_device,
@@ -44,6 +46,7 @@ __all__ = [
     "lib_path",
     "mla_combine",
     "mla_decode_paged",
+    "mla_decode_paged_noalloc",
     "mla_decode_sparse",
     "mla_get_metadata",
     "mla_get_metadata_device",

@@ -93,6 +93,9 @@ def _load():
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.c_float, vp, pinfo, vp, sz, vp, vp, vp, vp]
+    lib.mla_decode_paged_noalloc.restype = ctypes.c_int
+    lib.mla_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, ctypes.c_float, vp, pinfo, vp, vp, vp]
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [vp, pinfo, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
     lib.mla_combine_f16.restype = ctypes.c_int
@@ -344,6 +347,47 @@ def mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv: int, meta: Meta
     _check(rc, "mla_decode_paged")
     if stage == "split":
         return out, lse, workspace
+    return out, lse
+
+
+def mla_decode_paged_noalloc(q, kvcache, block_table, cache_seqlens, dv: int, meta: Metadata,
+                             causal: bool = False, softmax_scale: float | None = None,
+                             out=None, lse=None):
+    """Dense paged decode (bf16) whose split partials live in the library's
+    static device array: the C call allocates nothing.  Pass ``out`` and
+    ``lse`` to allocate nothing here either.  Returns (out, lse)."""
+    lib = _load()
+    _need(q.dim() == 4 and kvcache.dim() == 4, "q is [B, s_q, h_q, d_qk], kvcache [blocks, 64, h_kv, d_qk]")
+    _need(q.dtype == torch.bfloat16 and kvcache.dtype == torch.bfloat16, "q and kvcache must be bf16")
+    _need(q.is_cuda and kvcache.is_cuda and block_table.is_cuda and cache_seqlens.is_cuda,
+          "all tensors must be on the GPU")
+    _need(q.is_contiguous() and kvcache.is_contiguous() and block_table.is_contiguous()
+          and cache_seqlens.is_contiguous(), "tensors must be contiguous")
+    _need(block_table.dtype == torch.int32 and cache_seqlens.dtype == torch.int32,
+          "block_table and cache_seqlens must be int32")
+    _need(not meta.sparse, "metadata was built for sparse decode")
+    B, s_q, h_q, d_qk = q.shape
+    nblk, page, h_kv, _ = kvcache.shape
+    _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
+    _need(cache_seqlens.shape == (B,), "cache_seqlens must be [B]")
+    if not meta.device_built:
+        _need(meta.blocks_needed() <= block_table.shape[1],
+              "cache_seqlens of the metadata need more blocks than block_table has columns")
+    if softmax_scale is None:
+        softmax_scale = d_qk ** -0.5
+    if out is None:
+        out = torch.empty((B, s_q, h_q, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+    _need(out.shape == (B, s_q, h_q, dv) and out.dtype == q.dtype and out.is_contiguous(),
+          "out must be contiguous [B, s_q, h_q, dv] bf16")
+    _need(lse.shape == (B, s_q, h_q) and lse.dtype == torch.float32 and lse.is_contiguous(),
+          "lse must be contiguous fp32 [B, s_q, h_q]")
+    rc = lib.mla_decode_paged_noalloc(
+        _ptr(q), _ptr(kvcache), _ptr(block_table), _ptr(cache_seqlens), B, s_q, h_q, h_kv, d_qk,
+        dv, nblk, page, block_table.shape[1], 1 if causal else 0, float(softmax_scale),
+        _ptr(meta.meta_dev), ctypes.byref(meta.info), _ptr(out), _ptr(lse), _stream(q.device))
+    _check(rc, "mla_decode_paged_noalloc")
     return out, lse
 
 

@@ -25,7 +25,7 @@ ARCH = "gfx950"
 
 SOURCES = ["mla_sched.cpp", "mla_sched_dev.hip", "mla_api.cpp", "mla_splitkv.hip",
            "mla_splitkv_f16.hip", "mla_decode_576.hip", "mla_decode_512.hip", "mla_decode_576_f16.hip",
-           "mla_decode_512_f16.hip", "mla_combine.hip"]
+           "mla_decode_512_f16.hip", "mla_combine.hip", "mla_noalloc.hip"]
 
 # Packed-FP32 VALU ops are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -29,7 +29,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q, int32_t h_q,
                  int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
                  int32_t page_block_size, const int32_t* meta_dev, const mla_sched_info* info,
-                 void* workspace, size_t workspace_bytes, void* out, float* lse, bool fp8) {
+                 void* workspace, size_t workspace_bytes, void* out, float* lse, bool fp8,
+                 bool check_workspace) {
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || d_qk < 1 || dv < 1 || num_blocks < 0 ||
       page_block_size < 1)
     return set_error(MLA_E_INVAL, "decode: negative or zero shape");
@@ -59,7 +60,7 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
     return set_error(MLA_E_INVAL, "decode: q/kvcache/out need 16-byte, lse 4-byte alignment");
   if (num_blocks < 1) return set_error(MLA_E_INVAL, "decode: empty kvcache");
   const size_t need = mla_workspace_bytes(info, dv);
-  if (need > 0) {
+  if (need > 0 && check_workspace) {
     if (!workspace) return set_error(MLA_E_INVAL, "decode: metadata has splits, workspace is null");
     if (!aligned(workspace, 256)) return set_error(MLA_E_INVAL, "decode: workspace not 256-aligned");
     if (workspace_bytes < need)
@@ -69,8 +70,6 @@ int check_common(const void* q, const void* kvcache, int32_t batch, int32_t s_q,
   (void)h_q;
   return MLA_OK;
 }
-
-enum { kStageSplit = 1, kStageCombine = 2 };
 
 }  // namespace
 
@@ -205,7 +204,8 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
                       void* stream, int stages, bool fp8, bool f16) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
-                        meta_dev, info, workspace, workspace_bytes, out, lse, fp8);
+                        meta_dev, info, workspace, workspace_bytes, out, lse, fp8,
+                        !(stages & kStageValidateOnly));
   if (rc != MLA_OK || batch == 0) return rc;
   if (!block_table || !cache_seqlens) return set_error(MLA_E_INVAL, "decode_paged: null block_table/seqlens");
   if (bt_stride < 1) return set_error(MLA_E_INVAL, "decode_paged: bt_stride=%d", bt_stride);
@@ -238,6 +238,7 @@ int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_t
   kp.topk = 0;
   kp.causal = causal;
   kp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (stages & kStageValidateOnly) return MLA_OK;
   return launch(kp, info, d_qk, false, fp8, f16, workspace, dv, stream, stages);
 }
 
@@ -249,7 +250,7 @@ int decode_sparse_impl(const void* q, const void* kvcache, const int32_t* indice
                        void* out, float* lse, void* stream, int stages, bool fp8, bool f16) {
   clear_error();
   int rc = check_common(q, kvcache, batch, s_q, h_q, h_kv, d_qk, dv, num_blocks, page_block_size,
-                        meta_dev, info, workspace, workspace_bytes, out, lse, fp8);
+                        meta_dev, info, workspace, workspace_bytes, out, lse, fp8, true);
   if (rc != MLA_OK || batch == 0) return rc;
   if (!indices) return set_error(MLA_E_INVAL, "decode_sparse: null indices");
   if (topk < 1) return set_error(MLA_E_INVAL, "decode_sparse: topk=%d", topk);
@@ -292,7 +293,7 @@ int sparse_prefill_impl(const void* q, const void* kv, const int32_t* indices, i
   // the shared checks see the KV rows as ceil(s_kv / 64) pages of 64
   const int64_t pages = (int64_t(s_kv) + kPage - 1) / kPage;
   int rc = check_common(q, kv, s_q, 1, h_q, h_kv, d_qk, dv, int32_t(pages), kPage, meta_dev, info,
-                        workspace, workspace_bytes, out, lse, false);
+                        workspace, workspace_bytes, out, lse, false, true);
   if (rc != MLA_OK || s_q == 0) return rc;
   if (!indices) return set_error(MLA_E_INVAL, "sparse_prefill: null indices");
   if (topk < 1) return set_error(MLA_E_INVAL, "sparse_prefill: topk=%d", topk);

@@ -19,6 +19,20 @@ void clear_error();
 // ceil(rows / rows_per_group(rows)) workgroups.
 inline int32_t rows_per_group(int32_t rows) { return rows > 64 ? 128 : 64; }
 
+// Stages of a decode call (bit mask).  kStageValidateOnly runs every argument
+// check except the workspace's and enqueues nothing.
+enum { kStageSplit = 1, kStageCombine = 2, kStageValidateOnly = 4 };
+
+// Dense paged decode behind the mla_decode_paged* entry points: argument
+// checks, then the stages asked for on `stream`.
+int decode_paged_impl(const void* q, const void* kvcache, const int32_t* block_table,
+                      const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                      int32_t h_kv, int32_t d_qk, int32_t dv, int32_t num_blocks,
+                      int32_t page_block_size, int32_t bt_stride, int32_t causal,
+                      float softmax_scale, const int32_t* meta_dev, const mla_sched_info* info,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      void* stream, int stages, bool fp8, bool f16);
+
 int32_t default_num_parts(int32_t rows, int32_t num_cus);
 size_t metadata_capacity(int32_t num_units, int32_t target_parts);
 

@@ -224,6 +224,36 @@ def test_decode_paged_rejects_bad_arguments(lib):
     assert b"row_blocks" in lib.mla_last_error()
 
 
+def _paged_noalloc(lib, info, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, batch=2, s_q=1, h_q=16, h_kv=1, d_qk=576, dv=512,
+             nblk=8, page=64, bt_stride=4, causal=0, scale=0.04, meta=FAKE, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_paged_noalloc(a["q"], a["kv"], a["bt"], a["sl"], a["batch"], a["s_q"],
+                                        a["h_q"], a["h_kv"], a["d_qk"], a["dv"], a["nblk"],
+                                        a["page"], a["bt_stride"], a["causal"], a["scale"],
+                                        a["meta"], ctypes.byref(info), a["out"], a["lse"], None)
+
+
+def test_decode_paged_noalloc_checks_before_touching_the_gpu(lib):
+    """The allocation-free variant runs mla_decode_paged's checks, then its
+    own size limit, before any HIP call (so all of this runs without a GPU)."""
+    rc, meta, info = _raw_meta(lib, [64, 200], P=512, rows=16)
+    assert rc == 0 and info.total_slots > 0
+    assert _paged_noalloc(lib, info, h_kv=2) == -2
+    assert _paged_noalloc(lib, info, page=32) == -2
+    assert _paged_noalloc(lib, info, q=FAKE + 2) == -1
+    assert _paged_noalloc(lib, info, batch=3) == -1
+    assert _paged_noalloc(lib, info, causal=2) == -1
+    assert _paged_noalloc(lib, info, bt=None) == -1
+    assert _paged_noalloc(lib, info, batch=0) == 0           # nothing to do, nothing touched
+    # a schedule whose split partials exceed the static array is refused
+    rc, meta, info = _raw_meta(lib, [65536] * 4, P=1024, rows=128)
+    assert rc == 0
+    assert lib.mla_workspace_bytes(ctypes.byref(info), 512) > (128 << 20)
+    assert _paged_noalloc(lib, info, batch=4, h_q=128, nblk=4096, bt_stride=1024) == -3
+    assert b"static scratch" in lib.mla_last_error()
+
+
 def test_decode_sparse_rejects_bad_arguments(lib):
     cap = lib.mla_metadata_capacity(2, 8)
     meta = np.zeros(cap, dtype=np.int32)
