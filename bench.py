@@ -9,8 +9,9 @@ scheduler runs once per decode step and its metadata is reused by every layer
 (the pages' call pattern), so it is timed separately on the host
 (``metadata_us``); ``with_metadata`` reports the rate when every step also
 rebuilds and uploads the metadata.  The cache is rotated over enough copies
-that one step's working set is not served from the 256 MB Infinity Cache of
-the previous step.
+that the bytes read between two uses of one copy exceed 1 GiB, four times the
+256 MB Infinity Cache: a step's rows are never served from what earlier steps
+left there.
 
 Algorithmic work (what the method must do, not padded work):
   FLOP  = sum over (query row, visible key) of 2 * (d_qk + d_v)
@@ -20,10 +21,11 @@ Algorithmic work (what the method must do, not padded work):
           + sequence lengths.
 The split workspace traffic is overhead and is not counted.
 
-Prints one JSON line.  The step time is the whole decode (split-KV then
-combine) timed back to back between two HIP events; the per-kernel durations
-come from a second pass over the same steps with HIP events before, between
-and after the two kernels of every step, recorded on the stream they run on.
+Prints one JSON line.  ``ms_per_step`` is the whole decode (split-KV then
+combine) over K steps timed back to back between two HIP events; the combine
+is timed alone the same way and the split-KV time is the difference.
+``step_ms`` gives the min and median of at least 100 single steps, each its
+own graph replay between two events (rotating over the cache copies).
 """
 from __future__ import annotations
 
@@ -60,14 +62,16 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_work(case) -> dict:
-    """Integer accounting of the work the method must do (see module docstring)."""
+def algorithmic_work(case, batches=None) -> dict:
+    """Integer accounting of the work the method must do (see module
+    docstring), over every request or over the requests in ``batches``."""
     s_q, d_qk, d_v = case["s_q"], case["d_qk"], case["d_v"]
-    B = case["q"].shape[0]
+    bsel = list(range(case["q"].shape[0])) if batches is None else list(batches)
+    B = len(bsel)
     row_bytes = 656 if case.get("kv_fp8") else d_qk * 2
     if case["sparse"]:
         heads = case["active_h_q"]
-        idx = case["indices"]
+        idx = case["indices"][bsel]
         nrows = case["kvcache"].shape[0] * case["kvcache"].shape[1]
         valid = ((idx >= 0) & (idx < nrows)).sum().item()
         flop = valid * heads * 2 * (d_qk + d_v)
@@ -76,7 +80,7 @@ def algorithmic_work(case) -> dict:
         keys = valid
     else:
         heads = case["h_q"]
-        sl = case["cache_seqlens"].tolist()
+        sl = [int(case["cache_seqlens"][b]) for b in bsel]
         keys = 0
         for L in sl:
             for i in range(s_q):
@@ -90,35 +94,56 @@ def algorithmic_work(case) -> dict:
                 keys=keys)
 
 
-def cpu_baseline(case, min_seconds: float, max_passes: int = 64) -> dict:
-    """The FP64 oracle as it stands, on the host cores, over whole passes of
-    the workload (at least one, until ``min_seconds`` have elapsed)."""
-    import numpy as np  # noqa: F401
+def _oracle_rate(case, min_seconds: float, max_passes: int, batches=None):
+    """(TFLOPS, passes, seconds) of the oracle over whole passes of the
+    workload, or of the requests in ``batches`` only."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
-        cores = max([p["num_threads"] for p in blas] or [os.cpu_count() or 1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    work = algorithmic_work(case)
+    work = algorithmic_work(case, batches)
     passes, t0 = 0, time.perf_counter()
     while True:
         if case["sparse"]:
             oracle.ref_decode_sparse(case["q"], case["kvcache"], case["indices"], case["d_v"],
-                                     case["softmax_scale"], heads=range(case["active_h_q"]))
+                                     case["softmax_scale"], heads=range(case["active_h_q"]),
+                                     batches=batches)
         else:
             oracle.ref_decode_paged(case["q"], case["kvcache"], case["block_table"],
                                     case["cache_seqlens"], case["d_v"], case["causal"],
-                                    case["softmax_scale"])
+                                    case["softmax_scale"], batches=batches)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= max_passes:
             break
-    return {"value": round(work["flop"] * passes / dt / 1e12, 6), "unit": "TFLOPS",
-            "cores": int(cores), "kind": "oracle",
-            "sample": f"whole workload x {passes} pass(es), {dt:.1f} s, float64 numpy "
-                      f"(BLAS threads {cores}, host cpus {os.cpu_count()})"}
+    return work["flop"] * passes / dt / 1e12, passes, dt
+
+
+def cpu_baseline(case, min_seconds: float, max_passes: int = 64) -> dict:
+    """The FP64 oracle as it stands, on the host cores: whole passes of the
+    workload until ``min_seconds`` have elapsed with every BLAS thread, then a
+    bounded sample (the first requests, about a quarter of that time) with one
+    thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max([p["num_threads"] for p in blas] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        cores = os.cpu_count() or 1
+    rate, passes, dt = _oracle_rate(case, min_seconds, max_passes)
+    out = {"value": round(rate, 6), "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+           "sample": f"whole workload x {passes} pass(es), {dt:.1f} s, float64 numpy "
+                     f"(BLAS threads {cores}, host cpus {os.cpu_count()})"}
+    if threadpool_limits is not None:
+        # one thread: requests whose share of the work fits the time budget
+        per_pass = dt / passes * cores
+        B = int(case["q"].shape[0])
+        nb = max(1, min(B, int(B * (min_seconds / 4) / max(per_pass, 1e-9))))
+        with threadpool_limits(limits=1, user_api="blas"):
+            r1, p1, d1 = _oracle_rate(case, min_seconds / 4, 4, batches=range(nb))
+        out["single_thread"] = {"value": round(r1, 6), "unit": "TFLOPS", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"requests 0..{nb - 1} of {B} x {p1} pass(es), "
+                                          f"{d1:.1f} s, float64 numpy, BLAS threads 1"}
+    return out
 
 
 COPY_PROBE_BYTES = 256 << 20  # read once and written once by the copy probe
@@ -136,7 +161,17 @@ def copy_probe(torch, dev, reps: int = 3):
     del src, dst
 
 
-def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
+ROTATE_BYTES = 1 << 30  # bytes read between two uses of one cache copy
+MAX_COPIES = 16
+
+
+def rotation_copies(step_bytes: int) -> int:
+    """Cache copies so that the other copies' steps read >= ROTATE_BYTES
+    between two uses of one copy."""
+    return max(2, min(MAX_COPIES, 1 + math.ceil(ROTATE_BYTES / max(step_bytes, 1))))
+
+
+def bench_workload(k, steps: int, warmup: int, replays: int = 100,
                    probe: bool = False) -> dict:
     import torch
 
@@ -148,8 +183,7 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     dev = torch.device("cuda", 0)
     q = case["q"].to(dev)
     kv0 = case["kvcache"].to(dev)
-    pool_mb = kv0.numel() * kv0.element_size() / 2**20
-    copies = max(1, min(8, math.ceil(rotate_mb / max(pool_mb, 1e-9))))
+    copies = rotation_copies(work["bytes"])
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     bt = case["block_table"].to(dev)
     sl = case["cache_seqlens"].to(dev)
@@ -265,6 +299,27 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
     split_ms = ms_step - comb_ms
     del g_step
 
+    # single steps: one graph per cache copy, replayed in rotation, each
+    # replay timed on its own
+    graphs = []
+    for c in range(copies):
+        graphs.append(capture(lambda c=c: (split(kvs[c], meta), combine(meta))))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(replays)]
+    for i in range(copies):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    for i in range(replays):
+        evs[i][0].record()
+        graphs[i % copies].replay()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    singles = sorted(a.elapsed_time(b) for a, b in evs)
+    step_stats = {"replays": replays, "min": round(singles[0], 5),
+                  "median": round(singles[len(singles) // 2], 5),
+                  "max": round(singles[-1], 5)}
+    del graphs
+
     # rate with the scheduler and its upload inside every step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -294,7 +349,7 @@ def bench_workload(k, steps: int, warmup: int, rotate_mb: int = 600,
         sched=dict(num_parts=meta.num_parts, row_blocks=meta.row_blocks,
                    max_splits=meta.max_splits, split_units=meta.num_split_units,
                    workspace_mb=round(ws_bytes / 2**20, 2)),
-        copies=copies,
+        copies=copies, step_stats=step_stats,
     )
     return res
 
@@ -322,7 +377,9 @@ def bench_prefill(steps: int, warmup: int, probe: bool = False) -> dict:
     case = make_config("p")
     work = prefill_work(case)
     dev = torch.device("cuda", 0)
-    q, kv, idx = case["q"].to(dev), case["kv"].to(dev), case["indices"].to(dev)
+    q, kv0, idx = case["q"].to(dev), case["kv"].to(dev), case["indices"].to(dev)
+    copies = rotation_copies(work["bytes"])
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     meta = mla.mla_get_metadata(np.zeros(case["s_q"], np.int32), 1, case["h_q"], topk=case["topk"],
                                 device=dev)
     out = torch.empty((case["s_q"], case["h_q"], case["d_v"]), dtype=torch.bfloat16, device=dev)
@@ -330,24 +387,26 @@ def bench_prefill(steps: int, warmup: int, probe: bool = False) -> dict:
     lse = torch.empty_like(mx)
     ws = torch.empty(max(meta.workspace_bytes(case["d_v"]), 256), dtype=torch.uint8, device=dev)
 
-    def run():
-        mla.mla_sparse_prefill(q, kv, idx, case["softmax_scale"], dv=case["d_v"], meta=meta,
-                               workspace=ws, out=out, max_logits=mx, lse=lse)
+    def run(i):
+        mla.mla_sparse_prefill(q, kvs[i % copies], idx, case["softmax_scale"], dv=case["d_v"],
+                               meta=meta, workspace=ws, out=out, max_logits=mx, lse=lse)
 
-    for _ in range(warmup):
-        run()
+    for i in range(warmup):
+        run(i)
     torch.cuda.synchronize()
     if probe:
         copy_probe(torch, dev)
     # untimed calls for at least 0.2 s first, as for the decode timings
     t_settle = time.perf_counter()
+    i = 0
     while time.perf_counter() - t_settle < 0.2:
-        run()
+        run(i)
+        i += 1
         torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
-        run()
+    for i in range(steps):
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -359,6 +418,7 @@ def bench_prefill(steps: int, warmup: int, probe: bool = False) -> dict:
                               unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None),
                 schedule=dict(num_parts=meta.num_parts, row_blocks=meta.row_blocks,
                               max_splits=meta.max_splits, split_units=meta.num_split_units),
+                cache_copies_rotated=copies,
                 note="split-KV and combine of one call, timed together")
 
 
@@ -419,6 +479,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replays", type=int, default=100,
+                    help="single steps timed one by one for step_ms (min / median)")
     ap.add_argument("--workload", default="2", choices=["1", "2", "3", "4", "5", "4f", "5f", "p"],
                     help="seeded workload (2 = varlen decode, h_q=128: the headline; 4f/5f: "
                          "FP8-cache variants of 4/5; p: the sparse prefill chunk)")
@@ -454,7 +516,7 @@ def main():
         print(json.dumps(dict(o, kernel_source_hash=kernel_hash())), flush=True)
         return
     k = int(args.workload) if args.workload.isdigit() else args.workload
-    r = bench_workload(k, args.steps, args.warmup, probe=args.copy_probe)
+    r = bench_workload(k, args.steps, args.warmup, replays=args.replays, probe=args.copy_probe)
     case = r["case"]
     r["roofline"]["traffic"] = load_traffic(k)
     line = {
@@ -465,6 +527,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_step"], 5),
+        "step_ms": r["step_stats"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -497,10 +560,12 @@ def main():
             others["p"]["roofline"]["traffic"] = load_traffic("p")
             torch.cuda.empty_cache()
             continue
-        o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2))
+        o = bench_workload(k, max(10, args.steps // 2), max(3, args.warmup // 2),
+                           replays=args.replays)
         o["roofline"]["traffic"] = load_traffic(k)
         others[str(k)] = {
             "workload": o["case"]["name"], "ms_per_step": round(o["ms_step"], 5),
+            "step_ms": o["step_stats"], "cache_copies_rotated": o["copies"],
             "tflops": round(o["tflops"], 2), "hbm_gbps": round(o["gbs"], 1),
             "frac_mfma_peak": round(o["tflops"] / PEAK_BF16_TFLOPS, 4),
             "frac_hbm_peak": round(o["gbs"] / PEAK_HBM_GBS, 4),
