@@ -637,8 +637,21 @@ void mla_splitkv(SplitKVParams p) {
   // gather_slice(i) issues slice i of the next tile's gather (between QK
   // k-steps).
   // `xb`: the LDS area of the pair exchanges (P halves, row maxima and sums).
+  // A row group whose 32 rows all lie past the unit's rows (units of at most
+  // 32 rows, e.g. 16 active heads) has nothing to compute: it issues its share
+  // of the next gather and meets the two workgroup barriers of the tile.
+  const bool idle_rows = row0 >= p.rows;
   auto compute_tile = [&](const uint8_t* buf, int blk, uint64_t vmask, int next_q_unit,
                           uint8_t* xb) __attribute__((always_inline)) {
+    if (idle_rows) {
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int i = 0; i < NLW; ++i) gather_slice(i);
+      }
+      lds_barrier();  // the row maxima exchange
+      lds_barrier();  // the P exchange
+      return;
+    }
     s16x8* x_p = reinterpret_cast<s16x8*>(xb);                     // [wave][2][64]
     float* x_max = reinterpret_cast<float*>(xb + XP_BYTES);           // [wave][32]
     float* x_sum = reinterpret_cast<float*>(xb + XP_BYTES + XM_BYTES);  // [wave][32]
