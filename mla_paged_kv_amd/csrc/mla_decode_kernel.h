@@ -331,6 +331,22 @@ void mla_decode(SplitKVParams p) {
     }
   }
 
+  // Dense gathers: this lane's byte offset in the tile for each of its NLW
+  // loads (its row and chunk as in gather_one below), computed once.
+  int goff[SPARSE ? 1 : NLW];
+  if constexpr (!SPARSE) {
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int q0 = 64 * i;
+      const int tl = q0 / CPR;
+      const int bnd = (tl + 1) * CPR - q0;
+      const bool second = bnd < 64 && lane >= bnd;
+      const int f16 = 16 * ((second ? swz<CPR>(tl + 1) : swz<CPR>(tl)) ^ (2 * (wave & 1)));
+      const int in_row = ((q0 + lane) * 16 - (tl + (second ? 1 : 0)) * RSB) ^ f16;
+      goff[i] = (RPW * wave + tl + (second ? 1 : 0)) * RSB + in_row;
+    }
+  }
+
   // output row of this lane for unit u: dense rows are (query token, head)
   // pairs of a request, sparse units are single query tokens
   auto row_index = [&](int u, int r) __attribute__((always_inline)) -> size_t {
@@ -424,16 +440,17 @@ void mla_decode(SplitKVParams p) {
   // Wavefront w fills LDS rows 8w..8w+7 with NLW direct-to-LDS loads of 1 KB
   // (64 lanes x 16 bytes): load i covers LDS chunks 64 i + lane of those rows,
   // i.e. row tl = (64 i + lane) / CPR at chunk position c = (64 i + lane) %
-  // CPR, whose source chunk is c ^ f(row).  Every lane reads an in-bounds
-  // row: dense tails repeat the last cached token of the tile (masked out of
-  // the softmax); invalid sparse indices read row num_rows, past the end of
-  // the pool's buffer resource, which returns zeros (WIDE: the tile's first
-  // valid row), so a masked token always adds exactly zero.
+  // CPR, whose source chunk is c ^ f(row).  Rows past a dense tile's last
+  // valid row lie past the end of the tile's buffer resource and read as
+  // zeros; invalid sparse indices read row num_rows, past the end of the
+  // pool's buffer resource, which also returns zeros (WIDE: the tile's first
+  // valid row).  Such tokens are masked out of the softmax, and a zero row
+  // adds exactly zero.
   constexpr int ROWB = RSB;
   struct Plan {
     int phys;  // dense: physical page; sparse: unused
     int r0;    // dense: first tile row in the page (0 or 32)
-    int tmax;  // dense: last valid row of the tile (rows past it are clamped)
+    int tmax;  // dense: last valid row of the tile (rows past it read as zeros)
     int idx;   // sparse: this lane's row index (lanes 0..31; substituted)
     uint32_t vmask;  // sparse: valid tokens of the tile (bit t)
   };
@@ -456,30 +473,34 @@ void mla_decode(SplitKVParams p) {
     }
     return g;
   };
-  auto page_rsrc = [&](int phys) __attribute__((always_inline)) {
-    const uint8_t* pg = reinterpret_cast<const uint8_t*>(p.kv) + size_t(phys) * kPage * ROWB;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, kPage * ROWB, kBufferWord3);
+  // a dense tile's valid rows: the resource starts at the tile's first row and
+  // ends after its last valid one, so a load of a row past it returns zeros
+  // (masked out of the softmax, and zero rows add exactly nothing)
+  auto tile_rsrc = [&](const Plan& g) __attribute__((always_inline)) {
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>(p.kv) + size_t(g.phys) * kPage * ROWB +
+                        size_t(g.r0) * ROWB;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, (g.tmax + 1) * ROWB,
+                                            kBufferWord3);
   };
   // the whole pool (sparse rows, pools whose byte size plus one row fits 32 bits)
   auto pool_rsrc = [&]() __attribute__((always_inline)) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), 0,
                                             int(uint32_t(p.num_rows) * uint32_t(ROWB)), kBufferWord3);
   };
-  // Load i of this wavefront's share of tile plan g into buffer dst.  `ln` is
-  // the lane id through an opaque copy, so the few offset operations are
-  // recomputed per tile instead of keeping NLW offsets alive.
+  // Load i of this wavefront's share of tile plan g into buffer dst.  Dense:
+  // the lane's offset in the tile is fixed (goff, computed once).  Sparse:
+  // `ln` is the lane id through an opaque copy, so the few offset operations
+  // are recomputed per tile instead of keeping NLW offsets alive.
   auto gather_one = [&](const Plan& g, int dst, int i, int ln) __attribute__((always_inline)) {
-    const int q0 = 64 * i;
-    const int tl = q0 / CPR;                 // first row of the load (within the wave's 8)
-    const int bnd = (tl + 1) * CPR - q0;     // first lane of row tl + 1 (>= 64: none)
-    const bool second = bnd < 64 && ln >= bnd;
-    const int t = RPW * wave + tl + (second ? 1 : 0);  // tile row of this lane
-    // swizzle of row t: the row's bit 3 is wave bit 0 (RPW = 8)
-    const int fw = 2 * (wave & 1);
-    const int f16 = 16 * ((second ? swz<CPR>(tl + 1) : swz<CPR>(tl)) ^ fw);
     const uint32_t to = lds_base + uint32_t(dst + (NLW * wave + i) * 1024);
-    const int in_row = ((q0 + ln) * 16 - (tl + (second ? 1 : 0)) * RSB) ^ f16;  // byte in the row
     if constexpr (SPARSE) {
+      const int q0 = 64 * i;
+      const int tl = q0 / CPR;                 // first row of the load (within the wave's 8)
+      const int bnd = (tl + 1) * CPR - q0;     // first lane of row tl + 1 (>= 64: none)
+      const bool second = bnd < 64 && ln >= bnd;
+      // swizzle of the lane's row: the row's bit 3 is wave bit 0 (RPW = 8)
+      const int f16 = 16 * ((second ? swz<CPR>(tl + 1) : swz<CPR>(tl)) ^ (2 * (wave & 1)));
+      const int in_row = ((q0 + ln) * 16 - (tl + (second ? 1 : 0)) * RSB) ^ f16;  // byte in the row
       const int r0 = __builtin_amdgcn_readlane(g.idx, RPW * wave + tl);
       const int r1 = bnd < 64 ? __builtin_amdgcn_readlane(g.idx, RPW * wave + tl + 1) : r0;
       const int r = second ? r1 : r0;
@@ -490,8 +511,8 @@ void mla_decode(SplitKVParams p) {
         dma_b128(pool_rsrc(), uint32_t(r) * uint32_t(RSB) + uint32_t(in_row), to);
       }
     } else {
-      const int tr = t > g.tmax ? g.tmax : t;  // clamp tail rows to the last valid one
-      dma_b128(page_rsrc(g.phys), uint32_t((g.r0 + tr) * RSB + in_row), to);
+      (void)ln;
+      dma_b128(tile_rsrc(g), uint32_t(goff[i]), to);
     }
   };
 
