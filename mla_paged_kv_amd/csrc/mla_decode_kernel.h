@@ -880,13 +880,20 @@ void mla_decode(SplitKVParams p) {
     for (int ct = 0; ct < NCT; ++ct) pin_agpr(acc[ct]);
     // Tile t0's loads (and the indices of t3) have landed; the loads of t1,
     // t2 (and the indices of t4, t5) may still be in flight.  At a segment
-    // start the queries loaded during the previous step (and the previous
-    // segment's output stores) are newer than all of them, so everything is
-    // waited for.
+    // start the queries were loaded during the previous step, after its QK
+    // product; every wavefront with a row to write then issued at least 64
+    // stores of the previous segment's output (and the slot load) after
+    // them, so waiting until at most 63 operations are in flight covers the
+    // queries and every older load without waiting for the stores.  (A
+    // wavefront whose rows all lie past the unit's never reads its queries'
+    // values into a result.)
     // (WIDE kernels spill registers to scratch, whose accesses share the
     // counter, so they always wait for everything.)
-    if (seg_start || WIDE)
+    static_assert(NCT * 4 >= 63, "a segment's output stores (4 per column tile) cover the wait");
+    if (WIDE)
       wait_vmem_n<0>();
+    else if (seg_start)
+      wait_vmem_n<63>();
     else
       wait_vmem_n<2 * NLW + 2>();
     q_landed();
