@@ -452,12 +452,13 @@ def _counter_rows(path: str, counter: str):
 def ingest_counters(k: int, fetch_csv: str, write_csv: str, command: str) -> dict:
     """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) of ``bench.py --workload k --copy-probe`` into HBM bytes per
-    split-KV launch.  Each counter is scaled by bytes / reading of the copy
+    split-KV launch (the pair kernel ``mla_splitkv`` or the decode kernel
+    ``mla_decode``, whichever the workload runs).  Each counter is scaled by bytes / reading of the copy
     probe in the same run (the neg kernel over COPY_PROBE_BYTES)."""
     out = {"workload": k, "kernel_hash": kernel_hash(), "command": command}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _counter_rows(path, counter)
-        split = [v for n, v in rows if "mla_splitkv" in n]
+        split = [v for n, v in rows if "mla_splitkv" in n or "mla_decode" in n]
         probe = [v for n, v in rows if "neg_kernel" in n]
         if not split or not probe:
             raise SystemExit(f"{path}: no split-KV or copy-probe dispatches with {counter}")
