@@ -133,16 +133,22 @@ def cpu_baseline(case, min_seconds: float, max_passes: int = 64) -> dict:
            "sample": f"whole workload x {passes} pass(es), {dt:.1f} s, float64 numpy "
                      f"(BLAS threads {cores}, host cpus {os.cpu_count()})"}
     if threadpool_limits is not None:
-        # one thread: requests whose share of the work fits the time budget
-        per_pass = dt / passes * cores
+        # one thread: requests 0, 1, ... (cycling) one at a time until a
+        # quarter of the time budget is spent (at least one request)
         B = int(case["q"].shape[0])
-        nb = max(1, min(B, int(B * (min_seconds / 4) / max(per_pass, 1e-9))))
+        flop, n, t1 = 0, 0, time.perf_counter()
         with threadpool_limits(limits=1, user_api="blas"):
-            r1, p1, d1 = _oracle_rate(case, min_seconds / 4, 4, batches=range(nb))
-        out["single_thread"] = {"value": round(r1, 6), "unit": "TFLOPS", "cores": 1,
+            while True:
+                _oracle_rate(case, 0.0, 1, batches=[n % B])
+                flop += algorithmic_work(case, [n % B])["flop"]
+                n += 1
+                if time.perf_counter() - t1 >= min_seconds / 4 or n >= 64 * B:
+                    break
+        d1 = time.perf_counter() - t1
+        out["single_thread"] = {"value": round(flop / d1 / 1e12, 6), "unit": "TFLOPS", "cores": 1,
                                 "kind": "oracle",
-                                "sample": f"requests 0..{nb - 1} of {B} x {p1} pass(es), "
-                                          f"{d1:.1f} s, float64 numpy, BLAS threads 1"}
+                                "sample": f"{n} requests (cycling over the {B}), {d1:.1f} s, float64 "
+                                          f"numpy, BLAS threads 1"}
     return out
 
 
