@@ -166,8 +166,9 @@ int mla_get_metadata(const int32_t* cache_seqlens_host, int32_t batch, int32_t s
  * Limits: at most 4096 units and 1024 parts (MLA_E_NOTSUP beyond).  A length
  * below 0 or above 2^24 cannot be reported to the host without a round trip:
  * the kernel then writes an empty schedule (num_parts = num_split_units = 0,
- * total_ints = -1 in the device header) and a decode call with it writes
- * nothing.  Other errors as for mla_get_metadata, plus MLA_E_HIP.
+ * total_ints = -1 in the device header, the unit and row counts kept) and a
+ * decode call with it writes O = 0 and LSE = NaN (max_logits NaN) into every
+ * output row.  Other errors as for mla_get_metadata, plus MLA_E_HIP.
  */
 int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int32_t batch, int32_t s_q,
                             int32_t h_q, int32_t h_kv, int32_t topk, int32_t active_h_q,
