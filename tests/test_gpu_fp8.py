@@ -8,7 +8,8 @@ counts and forced split counts), widely varying scales, sparse decode with
 invalid indices and active heads, NaN-poisoned bytes outside what a request
 may see, the split-KV + combine stages, the skewed long-context workload at
 full size (sampled requests) and the top-k sparse shape with a 576-wide FP8
-cache, and a sparse pool past 4 GiB (64-bit row addressing).
+cache, sparse pools past 4 GiB (64-bit row addressing) and between 2 and 4
+GiB (32-bit unsigned row offsets above 2^31).
 """
 import numpy as np
 import pytest
@@ -146,12 +147,12 @@ def test_fp8_sparse_topk2048_full_size():
     _check(case, num_parts=0, batches=list(range(0, 32, 5)), what="fp8 sparse topk 2048")
 
 
-@pytest.mark.parametrize("fp8,h_q", [(False, 16), (True, 16), (False, 128)])
-def test_sparse_pool_past_4gib(fp8, h_q):
-    """Rows beyond byte offset 2^32 of the pool: the 64-bit addressing path."""
+def _sparse_big_pool(fp8, h_q, gib):
+    """A sparse call over a pool of about `gib` GiB whose selected rows include
+    the pool's last 200000 (and a few invalid indices)."""
     row_bytes = 656 if fp8 else 1152
     d_qk = 576
-    n_rows = (int(4.6 * 2 ** 30) // row_bytes // 64 + 1) * 64
+    n_rows = (int(gib * 2 ** 30) // row_bytes // 64 + 1) * 64
     rng = np.random.default_rng(815)
     B, topk = 2, 300
     pos = np.sort(rng.choice(n_rows, size=(B, topk), replace=True), axis=1).astype(np.int64)
@@ -175,6 +176,19 @@ def test_sparse_pool_past_4gib(fp8, h_q):
     meta = metadata(case, num_parts=0)
     out, lse = run_gpu(d, meta)
     O, LSE = to_np(out, lse)
-    compare(O, LSE, *run_oracle(case), f"pool past 4 GiB fp8={fp8} h_q={h_q}")
+    compare(O, LSE, *run_oracle(case), f"pool of {gib} GiB fp8={fp8} h_q={h_q}")
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fp8,h_q", [(False, 16), (True, 16), (False, 128)])
+def test_sparse_pool_past_4gib(fp8, h_q):
+    """Rows beyond byte offset 2^32 of the pool: the 64-bit addressing path."""
+    _sparse_big_pool(fp8, h_q, 4.6)
+
+
+@pytest.mark.parametrize("fp8,h_q", [(False, 16), (True, 16), (False, 128)])
+def test_sparse_pool_between_2_and_4_gib(fp8, h_q):
+    """Rows beyond byte offset 2^31 of a pool below 4 GiB: the 32-bit buffer
+    offsets, which must be unsigned there."""
+    _sparse_big_pool(fp8, h_q, 3.3)
