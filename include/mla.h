@@ -93,8 +93,9 @@ const char* mla_strerror(int code);
 const char* mla_last_error(void);
 
 /* Default part count for `rows` query rows per unit on a device with `num_cus`
- * compute units: max(1, num_cus / ceil(rows / 64)), i.e. one part per
- * workgroup slot (64 rows per workgroup, one resident workgroup per CU). */
+ * compute units: max(1, num_cus / ceil(rows / G)), G = 128 if rows > 64 else
+ * 64, i.e. one part per workgroup slot (G rows per workgroup, one resident
+ * workgroup per CU). */
 int32_t mla_default_num_parts(int32_t rows, int32_t num_cus);
 
 /* Upper bound, in int32, of the metadata for `num_units` units and at most
