@@ -146,16 +146,51 @@ __device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t rs, uint32_t voff
   asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
                : "memory");
 }
-// A 16-byte global load into a register tuple the compiler already holds
-// ("+v": the loaded value lands in the registers of the value it replaces,
-// so the register allocator never moves it while it is in flight).  Like the
-// direct-to-LDS loads it is invisible to the compiler's waits: the kernel
-// waits for it (s_waitcnt vmcnt(0) before the first use) and then redefines
-// the registers with an empty asm statement.
-template <typename T>
-__device__ __forceinline__ void load_b128(T& dst, const void* src) {
-  asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(dst) : "v"(src) : "memory");
+// N query fragments of 16 bytes at a 32-byte stride, loaded and waited for
+// in one statement: the registers are written before the statement ends, so
+// no load into a register is ever in flight outside it (early-clobber
+// outputs keep the address register apart from them).  Compiler-visible
+// loads instead would be waited for by counts that leave out the
+// direct-to-LDS loads issued after them, and the compiler would drain every
+// gather in flight before the QK product of every tile.  The closing
+// vmcnt(0) also waits for every older load: the tile gathers in flight at a
+// segment change land before the next segment starts.
+#define QO(i) "=&v"(d[i])
+template <int N>
+__device__ __forceinline__ void load_q_half(bf16x8* d, const uint16_t* src) {
+  static_assert(N == 18 || N == 16, "18 (d_qk 576) or 16 (d_qk 512) fragments");
+  if constexpr (N == 18) {
+    asm volatile(
+        "global_load_dwordx4 %0, %18, off offset:0\n\tglobal_load_dwordx4 %1, %18, off offset:32\n\t"
+        "global_load_dwordx4 %2, %18, off offset:64\n\tglobal_load_dwordx4 %3, %18, off offset:96\n\t"
+        "global_load_dwordx4 %4, %18, off offset:128\n\tglobal_load_dwordx4 %5, %18, off offset:160\n\t"
+        "global_load_dwordx4 %6, %18, off offset:192\n\tglobal_load_dwordx4 %7, %18, off offset:224\n\t"
+        "global_load_dwordx4 %8, %18, off offset:256\n\tglobal_load_dwordx4 %9, %18, off offset:288\n\t"
+        "global_load_dwordx4 %10, %18, off offset:320\n\tglobal_load_dwordx4 %11, %18, off offset:352\n\t"
+        "global_load_dwordx4 %12, %18, off offset:384\n\tglobal_load_dwordx4 %13, %18, off offset:416\n\t"
+        "global_load_dwordx4 %14, %18, off offset:448\n\tglobal_load_dwordx4 %15, %18, off offset:480\n\t"
+        "global_load_dwordx4 %16, %18, off offset:512\n\tglobal_load_dwordx4 %17, %18, off offset:544\n\t"
+        "s_waitcnt vmcnt(0)"
+        : QO(0), QO(1), QO(2), QO(3), QO(4), QO(5), QO(6), QO(7), QO(8), QO(9), QO(10), QO(11),
+          QO(12), QO(13), QO(14), QO(15), QO(16), QO(17)
+        : "v"(src) : "memory");
+  } else {
+    asm volatile(
+        "global_load_dwordx4 %0, %16, off offset:0\n\tglobal_load_dwordx4 %1, %16, off offset:32\n\t"
+        "global_load_dwordx4 %2, %16, off offset:64\n\tglobal_load_dwordx4 %3, %16, off offset:96\n\t"
+        "global_load_dwordx4 %4, %16, off offset:128\n\tglobal_load_dwordx4 %5, %16, off offset:160\n\t"
+        "global_load_dwordx4 %6, %16, off offset:192\n\tglobal_load_dwordx4 %7, %16, off offset:224\n\t"
+        "global_load_dwordx4 %8, %16, off offset:256\n\tglobal_load_dwordx4 %9, %16, off offset:288\n\t"
+        "global_load_dwordx4 %10, %16, off offset:320\n\tglobal_load_dwordx4 %11, %16, off offset:352\n\t"
+        "global_load_dwordx4 %12, %16, off offset:384\n\tglobal_load_dwordx4 %13, %16, off offset:416\n\t"
+        "global_load_dwordx4 %14, %16, off offset:448\n\tglobal_load_dwordx4 %15, %16, off offset:480\n\t"
+        "s_waitcnt vmcnt(0)"
+        : QO(0), QO(1), QO(2), QO(3), QO(4), QO(5), QO(6), QO(7), QO(8), QO(9), QO(10), QO(11),
+          QO(12), QO(13), QO(14), QO(15)
+        : "v"(src) : "memory");
+  }
 }
+#undef QO
 __device__ __forceinline__ void dma_global_b128(const void* src, uint32_t lds_addr) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
 }
@@ -540,26 +575,19 @@ void mla_decode(SplitKVParams p) {
     m_exact = -__builtin_inff();
     l_run = 0.f;
   };
-  // rows past the unit's last row read that last row (never written back);
-  // the loads are waited for at the start of the segment's first step
-  // (WIDE kernels spill registers, and a spill could copy the registers of a
-  // load still in flight, so their loads are the compiler's own; they wait
-  // for everything at every step anyway.)
+  // rows past the unit's last row read that last row (never written back).
+  // WIDE kernels spill registers, so their loads are the compiler's own (they
+  // wait for everything at every step anyway).
   auto load_q = [&](int u) __attribute__((always_inline)) {
     const uint16_t* qp = p.q + row_index(u, row_ok ? row : p.rows - 1) * D_QK + 8 * lgrp;
+    if constexpr (WIDE) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if constexpr (WIDE)
-        qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
-      else
-        load_b128(qf[kk], qp + kk * 16);
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+    } else {
+      static_assert(KK % 2 == 0, "two halves");
+#pragma unroll
+      for (int h = 0; h < 2; ++h) load_q_half<KK / 2>(qf + h * (KK / 2), qp + h * (KK / 2) * 16);
     }
-  };
-  // after a wait that covers the query loads: from here on the compiler may
-  // treat the registers as holding their values
-  auto q_landed = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[kk]));
   };
 
   // Writes the segment result of this lane's row (its NCOL columns): 16-bit O
@@ -881,22 +909,17 @@ void mla_decode(SplitKVParams p) {
     // Tile t0's loads (and the indices of t3) have landed; the loads of t1,
     // t2 (and the indices of t4, t5) may still be in flight.  At a segment
     // start the queries were loaded during the previous step, after its QK
-    // product; every wavefront with a row to write then issued at least 64
-    // stores of the previous segment's output (and the slot load) after
-    // them, so waiting until at most 63 operations are in flight covers the
-    // queries and every older load without waiting for the stores.  (A
-    // wavefront whose rows all lie past the unit's never reads its queries'
-    // values into a result.)
+    // product, by a statement that waited for every older load (tile t0's
+    // and t3's indices among them); waiting until at most 63 operations are
+    // in flight then leaves the previous segment's output stores alone.
     // (WIDE kernels spill registers to scratch, whose accesses share the
     // counter, so they always wait for everything.)
-    static_assert(NCT * 4 >= 63, "a segment's output stores (4 per column tile) cover the wait");
     if (WIDE)
       wait_vmem_n<0>();
     else if (seg_start)
       wait_vmem_n<63>();
     else
       wait_vmem_n<2 * NLW + 2>();
-    q_landed();
     lds_barrier();
     const bool has_next = t1.s < seg_end;
     const Plan g3 = plan_tile(t3, read_slot(t3, (tnum + 3) % NISLOT));

@@ -50,6 +50,10 @@ def test_tiny_workload():
 @pytest.mark.parametrize("s_q,causal,h_q,d_qk", [
     (1, False, 16, 576), (1, False, 128, 576), (2, True, 64, 576), (3, True, 16, 576),
     (1, False, 24, 576), (2, False, 8, 512), (1, False, 128, 512),
+    # units of 96, 80 and 160 rows: 128-row workgroups with wavefronts whose
+    # 32 rows are all past the unit's, through segment changes (P = 1 walks
+    # every request in one part)
+    (3, True, 32, 576), (1, False, 80, 576), (5, True, 32, 576),
 ])
 def test_dense_ragged_multi_tile(s_q, causal, h_q, d_qk):
     lens = [1, 63, 64, 65, 700, 2, 130]
