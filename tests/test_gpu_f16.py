@@ -74,7 +74,7 @@ def test_f16_sparse_prefill():
     torch.cuda.synchronize()
     assert out.dtype == F16
     Or, Mr, Lr = ref_sparse_prefill(case["q"], case["kv"], case["indices"], case["softmax_scale"])
-    O = out.float().cpu().numpy().astype(np.float64)
+    O = out.double().cpu().numpy()
     rel = np.linalg.norm(O - Or) / np.linalg.norm(Or)
     lerr = np.abs(lse.cpu().numpy() - Lr).max()
     merr = np.abs(mx.cpu().numpy() - Mr).max()

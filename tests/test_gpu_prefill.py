@@ -36,8 +36,8 @@ def _run(case, num_parts=0):
     out, mx, lse = mla.mla_sparse_prefill(q, kv, idx, case["softmax_scale"], dv=case["d_v"],
                                           meta=meta)
     torch.cuda.synchronize()
-    return (out.float().cpu().numpy().astype(np.float64), mx.cpu().numpy().astype(np.float64),
-            lse.cpu().numpy().astype(np.float64))
+    return (out.double().cpu().numpy(), mx.double().cpu().numpy(),
+            lse.double().cpu().numpy())
 
 
 def _compare(got, ref, rows, what):
@@ -78,8 +78,8 @@ def test_prefill_all_invalid_queries_and_pages_call():
     out, mx, lse = mla.flash_mla_sparse_fwd(case["q"].cuda(), case["kv"].cuda(), idx.cuda(),
                                             case["softmax_scale"])
     torch.cuda.synchronize()
-    got = (out.float().cpu().numpy().astype(np.float64), mx.cpu().numpy().astype(np.float64),
-           lse.cpu().numpy().astype(np.float64))
+    got = (out.double().cpu().numpy(), mx.double().cpu().numpy(),
+           lse.double().cpu().numpy())
     ref = ref_sparse_prefill(case["q"], case["kv"], idx, case["softmax_scale"])
     _compare(got, ref, slice(None), "all-invalid rows")
     assert np.all(np.isneginf(got[2][[2, 5]]))
