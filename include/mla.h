@@ -191,7 +191,9 @@ size_t mla_workspace_bytes(const mla_sched_info* info, int32_t d_v);
  *   kvcache        [num_blocks, page_block_size, h_kv, d_qk] bf16, device.
  *   block_table    [batch, bt_stride] int32, device.  Entries for logical
  *                  blocks below ceil(cache_seqlens[b] / 64) must be in
- *                  [0, num_blocks); other entries are never read.
+ *                  [0, num_blocks); other entries are never read.  Any
+ *                  size: a table of 2 GiB or more runs units of more than 64
+ *                  query rows on the 64-row kernel (slower, same results).
  *   cache_seqlens  [batch] int32, device; the same values the metadata was
  *                  built from.  Must be <= bt_stride * 64.
  *   dv             value width (first dv columns of each cache row).
@@ -224,7 +226,8 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
  *                  addressed as [num_blocks * page_block_size, h_kv, d_qk].
  *   indices        [batch, s_q, topk] int32, device: block * 64 + offset.  An
  *                  entry < 0 or >= num_blocks * 64 is invalid and skipped; no
- *                  block table is needed.
+ *                  block table is needed.  Any size, as for the block table
+ *                  of mla_decode_paged.
  *   meta_dev, info from mla_get_metadata in sparse mode (topk > 0) with the
  *                  same batch, s_q, h_q, topk; its active head count decides
  *                  which heads are computed (the first ones).

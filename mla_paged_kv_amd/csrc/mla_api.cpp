@@ -141,9 +141,15 @@ int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool spa
   if (stages & kStageSplit) {
     // units of more than 64 rows: the decode kernel (each wavefront owns 32
     // rows and all 512 output columns, 128 rows per workgroup); otherwise, and
-    // for the FP8 cache, the pair kernel
-    const hipError_t e = (fp8 || kp.rows <= 64) ? launch_pairs(kp, d_qk, sparse, fp8, f16, st)
-                                                : launch_decode(kp, d_qk, sparse, f16, st);
+    // for the FP8 cache, the pair kernel.  The decode kernel reads the block
+    // table (dense) or the index lists (sparse) through one buffer resource
+    // with 32-bit byte offsets below 2^31; a larger table goes to the pair
+    // kernel, which addresses it with 64-bit pointers.
+    const int64_t table_ints = int64_t(info->num_units) * (sparse ? kp.topk : kp.bt_stride);
+    const bool table_fits = table_ints <= int64_t(INT32_MAX / 4);
+    const hipError_t e = (fp8 || kp.rows <= 64 || !table_fits)
+                             ? launch_pairs(kp, d_qk, sparse, fp8, f16, st)
+                             : launch_decode(kp, d_qk, sparse, f16, st);
     if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
   if (stages & kStageCombine)
