@@ -862,9 +862,6 @@ void mla_decode(SplitKVParams p) {
     return n.s < seg_end ? n : Tile{seg_end, prev.pos, prev.u, prev.b1, prev.len};
   };
   Tile t0 = first_tile_from(cs0);
-  load_q(t0.u);
-  zero_acc();
-  n_vis = SPARSE ? 0 : visible(t0.len);
   Tile t1 = clamp_end(next_tile(t0), t0);
   Tile t2 = clamp_end(next_tile(t1), t1);
   Tile t3 = clamp_end(next_tile(t2), t2);
@@ -872,11 +869,16 @@ void mla_decode(SplitKVParams p) {
   Tile t5 = clamp_end(next_tile(t4), t4);
   uint32_t vm0, vm1, vm2;
   {
-    // the slots of tiles 0..2 are needed now; those of 3..5 follow the
-    // gathers of 0..2 in the steady-state order
+    // The slots of tiles 0..2 are needed now: their loads go out first, and
+    // the query loads' closing wait covers them too (one round trip for
+    // both).  Those of 3..5 follow the gathers of 0..2 in the steady-state
+    // order.
     load_slot(t0, 0);
     load_slot(t1, 1);
     load_slot(t2, 2);
+    load_q(t0.u);
+    zero_acc();
+    n_vis = SPARSE ? 0 : visible(t0.len);
     wait_vmem_n<0>();
     lds_barrier();
     int ln = lane;
