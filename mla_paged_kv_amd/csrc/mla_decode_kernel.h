@@ -590,6 +590,39 @@ void mla_decode(SplitKVParams p) {
     }
   };
 
+  // The first segment's queries, when the workgroup's rows are consecutive
+  // rows of q (always, except for a dense call with fewer heads than h_q and
+  // several query tokens): wavefront w copies the 32 rows of its row group
+  // into tile buffer w with 1 KB direct-to-LDS loads laid out like a tile
+  // (chunk c of row t at c ^ f(t); rows past the unit's last one read zeros),
+  // and after the wait reads its fragments back with the K-read addresses.
+  // Each load fetches 1 KB of consecutive bytes, where the register loads of
+  // a segment change fetch 32 bytes from each of 32 rows: the prologue's
+  // burst of query loads from every workgroup at once takes several times
+  // longer that way.
+  static_assert(kWaves / WPR <= kBufs && kRowsWave == kTile, "a row group's queries fill one tile buffer");
+  auto gather_q_block = [&](int u) __attribute__((always_inline)) {
+    const int r0 = rb * RB + rgrp * kRowsWave;  // first row of the wavefront's block
+    const int nvalid = p.rows - r0 < 0 ? 0 : (p.rows - r0 > kRowsWave ? kRowsWave : p.rows - r0);
+    const uint16_t* base = p.q + row_index(u, r0 < p.rows ? r0 : p.rows - 1) * D_QK;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, nvalid * RSB,
+                                                      kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < kWaves * NLW; ++i) {
+      const int q = 64 * i + lane;
+      const int t = q / CPR;
+      const int c = q - t * CPR;
+      dma_b128(rs, uint32_t(t * RSB + 16 * (c ^ swz<CPR>(t))),
+               lds_base + uint32_t(rgrp * TBUF + i * 1024));
+    }
+  };
+  auto read_q_block = [&]() __attribute__((always_inline)) {
+    const uint8_t* buf = lds + rgrp * TBUF;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(buf + kbase[kk % NKB] + kk * 32);
+  };
+
   // Writes the segment result of this lane's row (its NCOL columns): 16-bit O
   // and the LSE when the segment covers its unit (slot < 0), else fp32 O and
   // the base-2 LSE into workspace slot `slot`.  A row without any visible
@@ -869,18 +902,25 @@ void mla_decode(SplitKVParams p) {
   Tile t5 = clamp_end(next_tile(t4), t4);
   uint32_t vm0, vm1, vm2;
   {
-    // The slots of tiles 0..2 are needed now: their loads go out first, and
-    // the query loads' closing wait covers them too (one round trip for
-    // both).  Those of 3..5 follow the gathers of 0..2 in the steady-state
-    // order.
+    // The slots of tiles 0..2 and the first queries are loaded together (one
+    // round trip for both); the slots of 3..5 follow the gathers of 0..2 in
+    // the steady-state order.
+    const bool q_lds = !WIDE && (SPARSE || p.heads == p.h_q || p.s_q == 1);
     load_slot(t0, 0);
     load_slot(t1, 1);
     load_slot(t2, 2);
-    load_q(t0.u);
+    if (q_lds)
+      gather_q_block(t0.u);
+    else
+      load_q(t0.u);
     zero_acc();
     n_vis = SPARSE ? 0 : visible(t0.len);
     wait_vmem_n<0>();
     lds_barrier();
+    if (q_lds) {
+      read_q_block();
+      lds_barrier();  // every wavefront has its queries before the buffers are refilled
+    }
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const Plan g0 = plan_tile(t0, read_slot(t0, 0));
