@@ -25,7 +25,7 @@ ARCH = "gfx950"
 
 SOURCES = ["mla_sched.cpp", "mla_sched_dev.hip", "mla_api.cpp", "mla_splitkv.hip",
            "mla_splitkv_f16.hip", "mla_decode_576.hip", "mla_decode_512.hip", "mla_decode_576_f16.hip",
-           "mla_decode_512_f16.hip", "mla_combine.hip", "mla_noalloc.hip"]
+           "mla_decode_512_f16.hip", "mla_narrow.hip", "mla_combine.hip", "mla_noalloc.hip"]
 
 # Packed-FP32 VALU ops are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -46,8 +46,11 @@ def hipcc() -> str:
 # the 64-bit-address (WIDE) ones must be free of scratch.  The compiler's
 # resource remarks say so per kernel.
 DECODE_SOURCES = {"mla_decode_576.hip", "mla_decode_512.hip", "mla_decode_576_f16.hip",
-                  "mla_decode_512_f16.hip"}
+                  "mla_decode_512_f16.hip", "mla_narrow.hip"}
 _KERNEL = re.compile(r"Function Name: (_ZN3mla10mla_decodeILi(\d+)ELb([01])ELb([01])ELb([01])ELi(\d+)E\S*)")
+# the narrow kernel (units of at most 16 rows) is scratch-free too: a spill
+# inside its loop would be a memory round trip per tile
+_NARROW = re.compile(r"Function Name: (_ZN3mla10mla_narrowI\S*)")
 _SCRATCH = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
 
 
@@ -59,11 +62,15 @@ def check_scratch(remarks: str, src: str) -> int:
         if m:
             name, wide, seen = m.group(1), m.group(4) == "1", seen + 1
             continue
+        m = _NARROW.search(line)
+        if m:
+            name, wide, seen = m.group(1), False, seen + 1
+            continue
         m = _SCRATCH.search(line)
         if m and name is not None:
             if int(m.group(1)) > 0 and not wide:
                 raise RuntimeError(f"{src}: {name} uses {m.group(1)} bytes/lane of scratch; the "
-                                   "decode kernels' load ordering needs them scratch-free")
+                                   "decode and narrow kernels must be scratch-free")
             name = None
     return seen
 

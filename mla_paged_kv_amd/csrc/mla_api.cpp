@@ -145,11 +145,19 @@ int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool spa
     // table (dense) or the index lists (sparse) through one buffer resource
     // with 32-bit byte offsets below 2^31; a larger table goes to the pair
     // kernel, which addresses it with 64-bit pointers.
+    // Units of at most 16 rows (e.g. 16 active heads, one query token) go to
+    // the narrow kernel, one 16-row MFMA block per workgroup, when their
+    // sparse pool is addressable with 32-bit byte offsets.
     const int64_t table_ints = int64_t(info->num_units) * (sparse ? kp.topk : kp.bt_stride);
     const bool table_fits = table_ints <= int64_t(INT32_MAX / 4);
-    const hipError_t e = (fp8 || kp.rows <= 64 || !table_fits)
-                             ? launch_pairs(kp, d_qk, sparse, fp8, f16, st)
-                             : launch_decode(kp, d_qk, sparse, f16, st);
+    const bool pool32 = !sparse || (uint64_t(kp.num_rows) + 2) * uint64_t(d_qk) * 2 <= 0xFFFFFFFFull;
+    hipError_t e;
+    if (!fp8 && kp.rows <= 16 && pool32)
+      e = launch_narrow(kp, d_qk, sparse, f16, st);
+    else if (fp8 || kp.rows <= 64 || !table_fits)
+      e = launch_pairs(kp, d_qk, sparse, fp8, f16, st);
+    else
+      e = launch_decode(kp, d_qk, sparse, f16, st);
     if (e != hipSuccess) return set_error(MLA_E_HIP, "splitkv launch: %s", hipGetErrorString(e));
   }
   if (stages & kStageCombine)

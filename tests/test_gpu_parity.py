@@ -165,7 +165,11 @@ def test_nan_poisoned_tails_and_spare_blocks_do_not_leak():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_sparse_active_heads_bit_identical_to_all_heads():
+def test_sparse_active_heads_match_all_heads():
+    """Scheduling only the 16 active heads (units of 16 rows: the narrow kernel,
+    16-row MFMA blocks) and scheduling all 64 heads (the pair kernel) give the
+    active heads the same result up to fp32 reassociation; both also match the
+    oracle."""
     case = make_sparse_case(37, B=4, s_q=1, h_q=64, active_h_q=16, topk=512, cache_len=8192,
                             invalid_tail=25, d_qk=512, d_v=512)
     d = to_device(case)
@@ -175,11 +179,9 @@ def test_sparse_active_heads_bit_identical_to_all_heads():
         assert m16.rows == 16 and m64.rows == 64
         o16, l16 = run_gpu(d, m16)
         o64, l64 = run_gpu(d, m64)
-        if m16.segments[:, 1:3].tolist() == m64.segments[:, 1:3].tolist():
-            assert torch.equal(o16[:, :, :16], o64[:, :, :16])
-            assert torch.equal(l16[:, :, :16], l64[:, :, :16])
-        else:  # different split points: equal up to fp32 reassociation
-            assert (o16[:, :, :16].float() - o64[:, :, :16].float()).abs().max() < 2e-2
+        assert (o16[:, :, :16].float() - o64[:, :, :16].float()).abs().max() < 2e-2
+        assert (l16[:, :, :16] - l64[:, :, :16]).abs().max() < 1e-4
+    _check(case, num_parts=5, what="active heads only")
 
 
 def test_sparse_poisoned_invalid_rows_do_not_leak():
