@@ -428,6 +428,10 @@ def bench_prefill(steps: int, warmup: int, probe: bool = False) -> dict:
                 note="split-KV and combine of one call, timed together")
 
 
+# name stems of the split-KV kernels (one of them runs per workload)
+SPLIT_KERNELS = ("mla_splitkv", "mla_decode", "mla_narrow")
+
+
 def traffic_path(k) -> str:
     return os.path.join(ROOT, "profiles", f"splitkv_traffic_workload{k}.json")
 
@@ -458,13 +462,14 @@ def _counter_rows(path: str, counter: str):
 def ingest_counters(k: int, fetch_csv: str, write_csv: str, command: str) -> dict:
     """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) of ``bench.py --workload k --copy-probe`` into HBM bytes per
-    split-KV launch (the pair kernel ``mla_splitkv`` or the decode kernel
-    ``mla_decode``, whichever the workload runs).  Each counter is scaled by bytes / reading of the copy
+    split-KV launch (the pair kernel ``mla_splitkv``, the decode kernel
+    ``mla_decode`` or the narrow kernel ``mla_narrow``, whichever the workload
+    runs).  Each counter is scaled by bytes / reading of the copy
     probe in the same run (the neg kernel over COPY_PROBE_BYTES)."""
     out = {"workload": k, "kernel_hash": kernel_hash(), "command": command}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _counter_rows(path, counter)
-        split = [v for n, v in rows if "mla_splitkv" in n or "mla_decode" in n]
+        split = [v for n, v in rows if any(k in n for k in SPLIT_KERNELS)]
         probe = [v for n, v in rows if "neg_kernel" in n]
         if not split or not probe:
             raise SystemExit(f"{path}: no split-KV or copy-probe dispatches with {counter}")

@@ -107,3 +107,16 @@ def test_counter_ingestion_needs_both_kernels(tmp_path, monkeypatch):
     _write_counter_csv(f, "FETCH_SIZE", [("mla_splitkv<576>", "FETCH_SIZE", 1.0)])
     with pytest.raises(SystemExit):
         bench.ingest_counters(2, str(f), str(f), "cmd")
+
+
+def test_counter_ingestion_takes_the_narrow_kernel(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "traffic_path", lambda k: str(tmp_path / f"traffic{k}.json"))
+    probe_kib = bench.COPY_PROBE_BYTES / 1024
+    narrow = "void mla::mla_narrow<512, true, false, 2>(mla::SplitKVParams)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, neg_kernel_cuda>(...)"
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    _write_counter_csv(f, "FETCH_SIZE", [(neg, "FETCH_SIZE", probe_kib), (narrow, "FETCH_SIZE", 64.0)])
+    _write_counter_csv(w, "WRITE_SIZE", [(neg, "WRITE_SIZE", probe_kib), (narrow, "WRITE_SIZE", 8.0)])
+    out = bench.ingest_counters(5, str(f), str(w), "cmd")
+    assert out["traffic_bytes_per_launch"] == (64 + 8) * 1024
