@@ -146,14 +146,16 @@ int launch(SplitKVParams& kp, const mla_sched_info* info, int32_t d_qk, bool spa
     // with 32-bit byte offsets below 2^31; a larger table goes to the pair
     // kernel, which addresses it with 64-bit pointers.
     // Units of at most 16 rows (e.g. 16 active heads, one query token) go to
-    // the narrow kernel, one 16-row MFMA block per workgroup, when their
-    // sparse pool is addressable with 32-bit byte offsets.
+    // the narrow kernel, one 16-row MFMA block per workgroup (bf16, fp16 and
+    // FP8 caches), when their sparse pool is addressable with 32-bit byte
+    // offsets.
     const int64_t table_ints = int64_t(info->num_units) * (sparse ? kp.topk : kp.bt_stride);
     const bool table_fits = table_ints <= int64_t(INT32_MAX / 4);
-    const bool pool32 = !sparse || (uint64_t(kp.num_rows) + 2) * uint64_t(d_qk) * 2 <= 0xFFFFFFFFull;
+    const uint64_t row_bytes = fp8 ? uint64_t(kFp8RowBytes) : uint64_t(d_qk) * 2;
+    const bool pool32 = !sparse || (uint64_t(kp.num_rows) + 2) * row_bytes <= 0xFFFFFFFFull;
     hipError_t e;
-    if (!fp8 && kp.rows <= 16 && pool32)
-      e = launch_narrow(kp, d_qk, sparse, f16, st);
+    if (kp.rows <= 16 && pool32)
+      e = launch_narrow(kp, d_qk, sparse, fp8, f16, st);
     else if (fp8 || kp.rows <= 64 || !table_fits)
       e = launch_pairs(kp, d_qk, sparse, fp8, f16, st);
     else

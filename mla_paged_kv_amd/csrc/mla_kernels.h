@@ -65,9 +65,10 @@ hipError_t launch_pairs(const SplitKVParams& p, int d_qk, bool sparse, bool fp8,
                         hipStream_t stream);
 hipError_t launch_pairs_f16(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream);
 // The narrow kernel (mla_narrow_kernel.h; units of at most 16 query rows,
-// one 16-row MFMA block per workgroup): bf16 / fp16 caches, sparse pools whose
-// byte size fits 32-bit offsets.
-hipError_t launch_narrow(const SplitKVParams& p, int d_qk, bool sparse, bool f16, hipStream_t stream);
+// one 16-row MFMA block per workgroup): bf16 / fp16 / FP8-with-scale caches,
+// sparse pools whose byte size fits 32-bit offsets.
+hipError_t launch_narrow(const SplitKVParams& p, int d_qk, bool sparse, bool fp8, bool f16,
+                         hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -60,6 +60,9 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Uniform metadata reads go through the constant address space (scalar loads).
 typedef const __attribute__((address_space(4))) int32_t cint;
@@ -158,6 +161,21 @@ __device__ __forceinline__ void mfma_pv(f32x4& c, const s16x4& a, const s16x4& b
 // onto distinct bank groups.
 __host__ __device__ constexpr int vsw(int t) { return ((t & 7) << 1) | (t >> 3); }
 
+// 8 e4m3 values (byte i of x = value i) times their group's scale, each
+// product rounded to fp32 and then to bf16 (nearest even): the dequantized
+// values of the upstream FlashMLA README's "FP8 KV Cache" format.
+__device__ __forceinline__ bf16x8 dequant8(u32x2 x, float sc) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(x[e], false) * sc;
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(x[e], true) * sc;
+    w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+    w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin; each XCD gets a
 // contiguous run of parts, so neighbouring parts (often the pieces of one
 // request, with the same queries) share an L2.
@@ -173,16 +191,20 @@ __device__ __forceinline__ int logical_group(int id, int total) {
 
 // D_QK: cache row width (576 or 512); SPARSE: rows through top-k index lists
 // (pools whose byte size fits 32-bit offsets); F16: fp16 q, cache and output;
+// FP8: 656-byte "FP8 with scale" cache rows (d_qk 576, bf16 q), dequantized in
+// the registers they are loaded into, by the wavefront that owns their token;
 // DEPTH: tiles in flight per wavefront.
-template <int D_QK, bool SPARSE, bool F16, int DEPTH>
+template <int D_QK, bool SPARSE, bool F16, bool FP8, int DEPTH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_narrow(SplitKVParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using namespace nk;
   constexpr int NK = D_QK / 32;   // QK k-steps
   constexpr int NV = kDV / 32;    // k-steps holding the value columns
-  constexpr int ROWB = D_QK * 2;  // bytes of one cache row
+  constexpr int ROWB = FP8 ? kFp8RowBytes : D_QK * 2;  // bytes of one cache row
   static_assert(DEPTH >= 2 && DEPTH <= 4, "tiles in flight");
+  static_assert(!FP8 || (D_QK == 576 && !F16), "FP8 rows: 512 e4m3 + 64 bf16 RoPE values, bf16 q");
+  constexpr int NE = FP8 ? kDV / 32 : 1;  // FP8: k-steps held as e4m3 bytes (the value columns)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kXBytes];
   __shared__ float xstat[3][kWaves][kRows];  // per-wavefront row maxima, sums, exact maxima
 
@@ -326,7 +348,12 @@ void mla_narrow(SplitKVParams p) {
   };
 
   // ---- registers ----
-  bf16x8 kr[DEPTH][NK];  // tile rows in flight: chunk 4 ks + g of row r
+  // tile rows in flight (row r of the wavefront's 16): bf16 chunk 4 ks + g;
+  // FP8 rows: e4m3 bytes 32 ks + 8 g .. +7 of the value columns (kq), the
+  // row's 4 group scales (ksc) and the RoPE chunks 4 j + g (kr, j = ks - 16)
+  bf16x8 kr[DEPTH][FP8 ? NK - NE : NK];
+  u32x2 kq[DEPTH][NE];
+  f32x4 ksc[DEPTH];
   Tile sl_t[DEPTH];      // the tile each slot holds
   bool sl_ok[DEPTH];     // the slot holds a tile of the stream
   uint32_t sl_vm[DEPTH];  // sparse: valid rows of the wavefront's 16 (bit t)
@@ -381,10 +408,22 @@ void mla_narrow(SplitKVParams p) {
       rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, nrow * ROWB, kBufferWord3);
       off = uint32_t((kWaveRows * wave + r) * ROWB);
     }
-    off += uint32_t(16 * g);
+    if constexpr (FP8) {
+      // the scales first: the first k-step's dequant then waits for two loads
+      ksc[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + kDV, 0, 0));
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-      kr[s][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * ks, 0, 0));
+      for (int ks = 0; ks < NE; ++ks)
+        kq[s][ks] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 32 * ks + 8 * g, 0, 0));
+#pragma unroll
+      for (int j = 0; j < NK - NE; ++j)
+        kr[s][j] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + kDV + 16 + 16 * (4 * j + g), 0, 0));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks)
+        kr[s][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * ks + 16 * g, 0, 0));
+    }
     sl_t[s] = t;
     sl_ok[s] = ok;
   };
@@ -471,13 +510,25 @@ void mla_narrow(SplitKVParams p) {
     constexpr int s = decltype(S)::value;
     // S^T of the wavefront's 16 tokens x 16 query rows, one accumulation chain
     f32x4 st;  // st[j]: token 16 w + 4 g + j, query row r
+    if constexpr (FP8) {
+      // dequantized k-step by k-step; the value columns go to the V stage
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) mfma_qk<F16>(st, kr[s][ks], qf[ks], ks == 0);
-    mfma_wait_result(st);
-    // the value columns into the wavefront's V stage
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8 a = ks < NE ? dequant8(kq[s][ks < NE ? ks : 0], ksc[s][(ks < NE ? ks : 0) / 4])
+                                 : kr[s][ks < NE ? 0 : ks - NE];
+        mfma_qk<F16>(st, a, qf[ks], ks == 0);
+        if (ks < NV) *reinterpret_cast<bf16x8*>(vst + vw[ks & 3] + 64 * ks) = a;
+      }
+      mfma_wait_result(st);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < NV; ++ks)
-      *reinterpret_cast<bf16x8*>(vst + vw[ks & 3] + 64 * ks) = kr[s][ks];
+      for (int ks = 0; ks < NK; ++ks) mfma_qk<F16>(st, kr[s][ks], qf[ks], ks == 0);
+      mfma_wait_result(st);
+      // the value columns into the wavefront's V stage
+#pragma unroll
+      for (int ks = 0; ks < NV; ++ks)
+        *reinterpret_cast<bf16x8*>(vst + vw[ks & 3] + 64 * ks) = kr[s][ks];
+    }
     // the slot's registers are free from here: its refill must not be
     // scheduled above these reads of it (both would be live at once)
     __builtin_amdgcn_sched_barrier(0);
@@ -628,16 +679,24 @@ void mla_narrow(SplitKVParams p) {
 // Launches the narrow kernel (one 4-wavefront workgroup per part) for units of
 // at most 16 query rows.
 template <bool F16>
-hipError_t launch_narrow_t(const SplitKVParams& p, int d_qk, bool sparse, hipStream_t stream) {
+hipError_t launch_narrow_t(const SplitKVParams& p, int d_qk, bool sparse, bool fp8, hipStream_t stream) {
   if (p.num_parts <= 0) return hipSuccess;
   const dim3 grid(p.num_parts), block(256);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, p); };
+  if constexpr (!F16) {
+    if (fp8) {
+      // (a lighter ring -- 44 registers per tile -- leaves room for 3 tiles)
+      if (sparse) go(mla_narrow<576, true, false, true, 3>);
+      else go(mla_narrow<576, false, false, true, 3>);
+      return hipGetLastError();
+    }
+  }
   if (d_qk == 576) {
-    if (sparse) go(mla_narrow<576, true, F16, 2>);
-    else go(mla_narrow<576, false, F16, 2>);
+    if (sparse) go(mla_narrow<576, true, F16, false, 2>);
+    else go(mla_narrow<576, false, F16, false, 2>);
   } else {
-    if (sparse) go(mla_narrow<512, true, F16, 2>);
-    else go(mla_narrow<512, false, F16, 2>);
+    if (sparse) go(mla_narrow<512, true, F16, false, 2>);
+    else go(mla_narrow<512, false, F16, false, 2>);
   }
   return hipGetLastError();
 }

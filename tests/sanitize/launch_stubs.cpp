@@ -25,7 +25,7 @@ template hipError_t launch_decode_d<512, true>(const SplitKVParams&, bool, hipSt
 hipError_t launch_pairs(const SplitKVParams&, int, bool, bool, bool, hipStream_t) {
   reached("launch_pairs");
 }
-hipError_t launch_narrow(const SplitKVParams&, int, bool, bool, hipStream_t) {
+hipError_t launch_narrow(const SplitKVParams&, int, bool, bool, bool, hipStream_t) {
   reached("launch_narrow");
 }
 hipError_t launch_combine(const CombineParams&, hipStream_t) { reached("launch_combine"); }

@@ -64,10 +64,12 @@ def test_fp8_sparse(active, P):
     _check(case, num_parts=P, what=f"fp8 sparse active={active} P={P}")
 
 
-def test_fp8_poisoned_bytes_do_not_leak():
+@pytest.mark.parametrize("h_q", [16, 8])
+def test_fp8_poisoned_bytes_do_not_leak(h_q):
     """NaN codes and NaN scales in rows a request may not see (page tails,
-    spare pages) leave the result bit-identical."""
-    case = make_dense_case(807, B=3, s_q=2, h_q=16, seqlens=[70, 129, 1], causal=True,
+    spare pages) leave the result bit-identical (h_q = 16: units of 32 rows,
+    the pair kernel; h_q = 8: 16 rows, the narrow kernel)."""
+    case = make_dense_case(807, B=3, s_q=2, h_q=h_q, seqlens=[70, 129, 1], causal=True,
                            spare_frac=1.0, kv_fp8=True)
     d = to_device(case)
     meta = metadata(case, num_parts=4)
