@@ -133,32 +133,34 @@ def test_device_metadata_reuses_buffer_across_calls():
         np.testing.assert_array_equal(m.exact(), ref_schedule(lens.tolist(), P, 32))
 
 
-@pytest.mark.parametrize("P", [0, 1, 9, 64])
-def test_decode_with_device_metadata_dense(P):
-    case = make_dense_case(501, B=5, s_q=2, h_q=64, seqlens=[3000, 1, 700, 64, 1500], causal=True,
+# h_q = 8: units of 16 rows (the narrow kernel); 64: 128 rows (the decode kernel)
+@pytest.mark.parametrize("P,h_q", [(0, 64), (1, 64), (9, 64), (64, 64), (0, 8), (9, 8)])
+def test_decode_with_device_metadata_dense(P, h_q):
+    case = make_dense_case(501, B=5, s_q=2, h_q=h_q, seqlens=[3000, 1, 700, 64, 1500], causal=True,
                            spare_frac=0.2)
     d = to_device(case)
-    log(f"decode with device metadata, dense P={P}")
-    md = mla.mla_get_metadata_device(d["cache_seqlens"], 2, 64, num_parts=P)
+    log(f"decode with device metadata, dense P={P} h_q={h_q}")
+    md = mla.mla_get_metadata_device(d["cache_seqlens"], 2, h_q, num_parts=P)
     out, lse = run_gpu(d, md)
     O, LSE = to_np(out, lse)
-    compare(O, LSE, *run_oracle(case), f"device-meta dense P={P}")
+    compare(O, LSE, *run_oracle(case), f"device-meta dense P={P} h_q={h_q}")
     mh = metadata(case, num_parts=P)
     np.testing.assert_array_equal(md.exact(), mh.meta_host)
     oh, lh = run_gpu(d, mh)
     _assert_close(out, lse, oh, lh)
 
 
-@pytest.mark.parametrize("P", [0, 3])
-def test_decode_with_device_metadata_sparse(P):
-    case = make_sparse_case(503, B=4, s_q=2, h_q=64, active_h_q=32, topk=1024, cache_len=6000,
+# 32 active heads: the pair kernel; 16: the narrow kernel
+@pytest.mark.parametrize("P,active", [(0, 32), (3, 32), (0, 16), (3, 16)])
+def test_decode_with_device_metadata_sparse(P, active):
+    case = make_sparse_case(503, B=4, s_q=2, h_q=64, active_h_q=active, topk=1024, cache_len=6000,
                             invalid_tail=17)
     d = to_device(case)
-    log(f"decode with device metadata, sparse P={P}")
-    md = mla.mla_get_metadata_device(None, 2, 64, topk=1024, active_h_q=32, num_parts=P, batch=4)
+    log(f"decode with device metadata, sparse P={P} active={active}")
+    md = mla.mla_get_metadata_device(None, 2, 64, topk=1024, active_h_q=active, num_parts=P, batch=4)
     out, lse = run_gpu(d, md)
     O, LSE = to_np(out, lse)
-    compare(O, LSE, *run_oracle(case), f"device-meta sparse P={P}")
+    compare(O, LSE, *run_oracle(case), f"device-meta sparse P={P} active={active}")
 
 
 def test_graph_captured_step_replays_with_new_lengths():

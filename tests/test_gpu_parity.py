@@ -50,6 +50,8 @@ def test_tiny_workload():
 @pytest.mark.parametrize("s_q,causal,h_q,d_qk", [
     (1, False, 16, 576), (1, False, 128, 576), (2, True, 64, 576), (3, True, 16, 576),
     (1, False, 24, 576), (2, False, 8, 512), (1, False, 128, 512),
+    # units of 16 rows with causal masking (the narrow kernel)
+    (2, True, 8, 576),
     # units of 96, 80 and 160 rows: 128-row workgroups with wavefronts whose
     # 32 rows are all past the unit's, through segment changes (P = 1 walks
     # every request in one part)
@@ -63,10 +65,12 @@ def test_dense_ragged_multi_tile(s_q, causal, h_q, d_qk):
         _check(case, num_parts=P, what=f"ragged s_q={s_q} causal={causal} h_q={h_q} d={d_qk} P={P}")
 
 
-def test_empty_and_fully_masked_rows():
+@pytest.mark.parametrize("h_q", [16, 8])
+def test_empty_and_fully_masked_rows(h_q):
     # L = 0 (empty request), L = 1 with s_q = 2 causal (query 0 sees nothing),
-    # L = 65 with s_q = 2 causal (query 0's last tile is fully masked when split)
-    case = make_dense_case(9, B=4, s_q=2, h_q=16, seqlens=[0, 1, 65, 129], causal=True,
+    # L = 65 with s_q = 2 causal (query 0's last tile is fully masked when split);
+    # h_q = 8 gives units of 16 rows (the narrow kernel)
+    case = make_dense_case(9, B=4, s_q=2, h_q=h_q, seqlens=[0, 1, 65, 129], causal=True,
                            spare_frac=0.5)
     for P in (0, 1, 3, 9):
         _check(case, num_parts=P, what=f"empty/masked P={P}")
