@@ -63,6 +63,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // through the constant address space, so uniform reads become scalar loads
 // that do not share the vector-memory counter with the tile gathers.
 typedef const __attribute__((address_space(4))) int32_t cint;
+// a segment record (unit, first block, end block, slot), read as one scalar load
+typedef int32_t i32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef const __attribute__((address_space(4))) i32x4a cseg;
 __device__ __forceinline__ cint* as_const(const int32_t* ptr) { return (cint*)(uintptr_t)ptr; }
 
 constexpr int kTile = 32;      // tokens per tile (half a page / index chunk)
@@ -334,11 +337,16 @@ void mla_decode(SplitKVParams p) {
   cint* meta = as_const(p.meta);
   // the grid covers p.num_parts parts; the device header says how many exist
   // (header word 15 is -1 when the device scheduler rejected the lengths)
-  const bool meta_bad = meta[15] == -1;
-  if (part >= meta[0] && !meta_bad) return;
+  // The header words and the part's segment range are independent reads,
+  // requested together before anything branches on them (one memory round
+  // trip, not three).
+  const int h_parts = meta[0], h_segs = meta[12], h_status = meta[15];
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
-  cint* segs = meta + meta[12];
+  asm volatile("" ::"s"(h_parts), "s"(h_segs), "s"(h_status), "s"(seg_begin), "s"(seg_end));
+  const bool meta_bad = h_status == -1;
+  if (part >= h_parts && !meta_bad) return;
+  cint* segs = meta + h_segs;
 
   const int row = rb * RB + rgrp * kRowsWave + lrow;
   const bool row_ok = row < p.rows;
@@ -406,20 +414,26 @@ void mla_decode(SplitKVParams p) {
 
   // ---- the tile stream ----
   auto seg_u = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 0]; };
-  auto seg_b0 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 1]; };
-  auto seg_b1 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 2]; };
   auto seg_slot = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 3]; };
+  auto seg_rec = [&](int s) __attribute__((always_inline)) { return *(cseg*)(segs + 4 * s); };
   auto unit_len = [&](int u) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) return p.topk;
     else return as_const(p.seqlens)[u];
   };
   // first tile at or after segment s2 (segments without blocks are skipped;
   // their outputs are written when the stream passes them)
-  auto first_tile_from = [&](int s2) __attribute__((always_inline)) -> Tile {
-    while (s2 < seg_end && seg_b0(s2) == seg_b1(s2)) ++s2;
+  // first tile at or after segment s2 (whose record is rec, when s2 is a
+  // segment), skipping segments without tiles; each record is one load
+  auto first_tile_rec = [&](int s2, i32x4a rec) __attribute__((always_inline)) -> Tile {
+    while (s2 < seg_end && rec[1] == rec[2]) {
+      ++s2;
+      if (s2 < seg_end) rec = seg_rec(s2);
+    }
     if (s2 >= seg_end) return Tile{seg_end, 0, 0, 0, 1};
-    const int u = seg_u(s2), b0 = seg_b0(s2);
-    return Tile{s2, 2 * b0, u, seg_b1(s2), unit_len(u)};
+    return Tile{s2, 2 * rec[1], rec[0], rec[2], unit_len(rec[0])};
+  };
+  auto first_tile_from = [&](int s2) __attribute__((always_inline)) -> Tile {
+    return first_tile_rec(s2, s2 < seg_end ? seg_rec(s2) : i32x4a{0, 0, 0, 0});
   };
   // a block's second half exists unless the unit ends in its first half
   auto has_next_half = [&](const Tile& t) __attribute__((always_inline)) -> bool {
@@ -875,9 +889,11 @@ void mla_decode(SplitKVParams p) {
   // ---- the stream of the part ----
   // leading segments without tiles
   int cs0 = seg_begin;
-  while (cs0 < seg_end && seg_b0(cs0) == seg_b1(cs0)) {
-    write_empty(seg_u(cs0), seg_slot(cs0));
+  i32x4a rec0 = cs0 < seg_end ? seg_rec(cs0) : i32x4a{0, 0, 0, 0};
+  while (cs0 < seg_end && rec0[1] == rec0[2]) {
+    write_empty(rec0[0], rec0[3]);
     ++cs0;
+    if (cs0 < seg_end) rec0 = seg_rec(cs0);
   }
   if (cs0 >= seg_end) return;
 
@@ -894,7 +910,7 @@ void mla_decode(SplitKVParams p) {
   auto clamp_end = [&](const Tile& n, const Tile& prev) __attribute__((always_inline)) -> Tile {
     return n.s < seg_end ? n : Tile{seg_end, prev.pos, prev.u, prev.b1, prev.len};
   };
-  Tile t0 = first_tile_from(cs0);
+  Tile t0 = first_tile_rec(cs0, rec0);
   Tile t1 = clamp_end(next_tile(t0), t0);
   Tile t2 = clamp_end(next_tile(t1), t1);
   Tile t3 = clamp_end(next_tile(t2), t2);

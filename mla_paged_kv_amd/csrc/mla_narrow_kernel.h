@@ -66,6 +66,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Uniform metadata reads go through the constant address space (scalar loads).
 typedef const __attribute__((address_space(4))) int32_t cint;
+// a segment record (unit, first block, end block, slot), read as one scalar load
+typedef int32_t i32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef const __attribute__((address_space(4))) i32x4a cseg;
 __device__ __forceinline__ cint* as_const(const int32_t* ptr) { return (cint*)(uintptr_t)ptr; }
 
 constexpr int kRows = 16;                 // query rows per workgroup
@@ -217,16 +220,21 @@ void mla_narrow(SplitKVParams p) {
   cint* meta = as_const(p.meta);
   // the grid covers p.num_parts parts, the device header says how many exist
   // (fewer only when the metadata was built on the device; header word 15 is
-  // -1 when the device scheduler rejected the lengths)
-  const bool meta_bad = meta[15] == -1;
-  if (part >= meta[0] && !meta_bad) return;
+  // -1 when the device scheduler rejected the lengths).  The header words and
+  // the part's segment range are independent reads, requested together before
+  // anything branches on them (one memory round trip, not three).
+  const int h_parts = meta[0], h_segs = meta[12], h_status = meta[15];
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
-  cint* segs = meta + meta[12];
+  // (the launch parameters the next steps need are requested with them)
+  asm volatile("" ::"s"(h_parts), "s"(h_segs), "s"(h_status), "s"(seg_begin), "s"(seg_end),
+               "s"(p.rows), "s"(p.s_q), "s"(p.h_q), "s"(p.heads), "s"(p.topk), "s"(p.num_rows));
+  const bool meta_bad = h_status == -1;
+  if (part >= h_parts && !meta_bad) return;
+  cint* segs = meta + h_segs;
   auto seg_u = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 0]; };
-  auto seg_b0 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 1]; };
-  auto seg_b1 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 2]; };
   auto seg_slot = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 3]; };
+  auto seg_rec = [&](int s) __attribute__((always_inline)) { return *(cseg*)(segs + 4 * s); };
 
   const bool row_ok = r < p.rows;
   const int qr = row_ok ? r : p.rows - 1;  // rows past the unit's last read it (never written)
@@ -311,12 +319,16 @@ void mla_narrow(SplitKVParams p) {
   };
   int la_b1 = 0, la_u = 0;  // cached segment of the furthest tile looked up
   auto first_tile_from = [&](int s2) __attribute__((always_inline)) -> Tile {
-    while (s2 < seg_end && seg_b0(s2) == seg_b1(s2)) ++s2;  // segments without tiles
+    // segments without tiles are passed over; each record is one load
+    i32x4a rec = s2 < seg_end ? seg_rec(s2) : i32x4a{0, 0, 0, 0};
+    while (s2 < seg_end && rec[1] == rec[2]) {
+      ++s2;
+      if (s2 < seg_end) rec = seg_rec(s2);
+    }
     if (s2 >= seg_end) return Tile{seg_end, 0, 0, true};
-    la_u = seg_u(s2);
-    la_b1 = seg_b1(s2);
-    const int b0 = seg_b0(s2);
-    return Tile{s2, b0, la_u, b0 + 1 >= la_b1};
+    la_u = rec[0];
+    la_b1 = rec[2];
+    return Tile{s2, rec[1], la_u, rec[1] + 1 >= la_b1};
   };
   auto next_tile = [&](const Tile& t) __attribute__((always_inline)) -> Tile {
     if (t.s >= seg_end) return t;
@@ -594,16 +606,20 @@ void mla_narrow(SplitKVParams p) {
     seg_first = false;
   };
 
-  // leading segments without tiles
+  // leading segments without tiles (one scalar load per segment record)
   int cs0 = seg_begin;
-  while (cs0 < seg_end && seg_b0(cs0) == seg_b1(cs0)) {
-    write_empty(seg_u(cs0), seg_slot(cs0));
+  i32x4a rec0 = cs0 < seg_end ? seg_rec(cs0) : i32x4a{0, 0, 0, 0};
+  while (cs0 < seg_end && rec0[1] == rec0[2]) {
+    write_empty(rec0[0], rec0[3]);
     ++cs0;
+    if (cs0 < seg_end) rec0 = seg_rec(cs0);
   }
   if (cs0 >= seg_end) return;
 
   // prologue: the first segment's queries, the first DEPTH tiles
-  Tile nt = first_tile_from(cs0);
+  la_u = rec0[0];
+  la_b1 = rec0[2];
+  Tile nt{cs0, rec0[1], la_u, rec0[1] + 1 >= la_b1};
   Meta nmeta = fetch_meta(nt);
   load_q(nt.u);
   qrow = row_index(nt.u, r);

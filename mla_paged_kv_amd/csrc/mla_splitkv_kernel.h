@@ -70,6 +70,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // loads instead of vector loads that would share the vector memory counter
 // with the in-flight tile gathers.
 typedef const __attribute__((address_space(4))) int32_t cint;
+// a segment record (unit, first block, end block, slot), read as one scalar load
+typedef int32_t i32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef const __attribute__((address_space(4))) i32x4a cseg;
 __device__ __forceinline__ cint* as_const(const int32_t* ptr) { return (cint*)(uintptr_t)ptr; }
 
 constexpr int kPage = 64;          // tokens per tile (one page, or 64 sparse indices)
@@ -259,15 +262,19 @@ void mla_splitkv(SplitKVParams p) {
   // the grid covers p.num_parts parts, the device header says how many exist
   // (fewer only when the metadata was built on the device; header word 15 is
   // -1 when the device scheduler rejected the lengths)
-  const bool meta_bad = meta[15] == -1;
-  if (part >= meta[0] && !meta_bad) return;
+  // The header words and the part's segment range are independent reads,
+  // requested together before anything branches on them (one memory round
+  // trip, not three).
+  const int h_parts = meta[0], h_segs = meta[12], h_status = meta[15];
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
-  cint* segs = meta + meta[12];
+  asm volatile("" ::"s"(h_parts), "s"(h_segs), "s"(h_status), "s"(seg_begin), "s"(seg_end));
+  const bool meta_bad = h_status == -1;
+  if (part >= h_parts && !meta_bad) return;
+  cint* segs = meta + h_segs;
   auto seg_u = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 0]; };
-  auto seg_b0 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 1]; };
-  auto seg_b1 = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 2]; };
   auto seg_slot = [&](int s) __attribute__((always_inline)) { return segs[4 * s + 3]; };
+  auto seg_rec = [&](int s) __attribute__((always_inline)) { return *(cseg*)(segs + 4 * s); };
 
   const int row0 = rb * kRowsPerGroup + rgrp * kRows;
   const int row = row0 + lrow;
@@ -846,17 +853,20 @@ void mla_splitkv(SplitKVParams p) {
     bool last;
   };
   int la_u = 0, la_b1 = 0;  // cached segment
-  auto load_seg = [&](int s2) __attribute__((always_inline)) {
-    la_u = seg_u(s2);
-    la_b1 = seg_b1(s2);
+  // first tile at or after segment s2 (whose record is rec, when s2 is a
+  // segment), skipping segments without tiles; each record is one load
+  auto first_tile_rec = [&](int s2, i32x4a rec) __attribute__((always_inline)) -> Tile {
+    while (s2 < seg_end && rec[1] == rec[2]) {
+      ++s2;
+      if (s2 < seg_end) rec = seg_rec(s2);
+    }
+    if (s2 >= seg_end) return Tile{seg_end, 0, 0, true};
+    la_u = rec[0];
+    la_b1 = rec[2];
+    return Tile{s2, rec[1], la_u, rec[1] + 1 >= la_b1};
   };
   auto first_tile_from = [&](int s2) __attribute__((always_inline)) -> Tile {
-    // first tile at or after segment s2, skipping segments without tiles
-    while (s2 < seg_end && seg_b0(s2) == seg_b1(s2)) ++s2;
-    if (s2 >= seg_end) return Tile{seg_end, 0, 0, true};
-    load_seg(s2);
-    const int b0 = seg_b0(s2);
-    return Tile{s2, b0, la_u, b0 + 1 >= la_b1};
+    return first_tile_rec(s2, s2 < seg_end ? seg_rec(s2) : i32x4a{0, 0, 0, 0});
   };
   // the tile after t (t is in the cached segment)
   auto next_tile = [&](const Tile& t) __attribute__((always_inline)) -> Tile {
@@ -885,14 +895,16 @@ void mla_splitkv(SplitKVParams p) {
 
   // leading segments without tiles
   int cs0 = seg_begin;
-  while (cs0 < seg_end && seg_b0(cs0) == seg_b1(cs0)) {
-    write_segment(row_index(seg_u(cs0), row), seg_slot(cs0), true);
+  i32x4a rec0 = cs0 < seg_end ? seg_rec(cs0) : i32x4a{0, 0, 0, 0};
+  while (cs0 < seg_end && rec0[1] == rec0[2]) {
+    write_segment(row_index(rec0[0], row), rec0[3], true);
     ++cs0;
+    if (cs0 < seg_end) rec0 = seg_rec(cs0);
   }
   if (cs0 >= seg_end) return;
 
   // first tile: gathered into buf_a before the stream starts
-  Tile ct = first_tile_from(cs0);
+  Tile ct = first_tile_rec(cs0, rec0);
   uint64_t cmask;
   const TileMeta m0 = fetch_meta(ct.u, ct.blk);
   {
