@@ -329,6 +329,12 @@ void mla_decode(SplitKVParams p) {
   const int lrow = lane & 31;               // query row owned within the row group
   const int lgrp = lane >> 5;               // k-group of the MFMA operands
 
+  // the metadata pointer, the shape words and the output pointers are
+  // requested with the launch's part count, so the header reads below do not
+  // wait for further rounds of argument loads
+  asm volatile("" ::"s"(p.meta), "s"(p.num_parts), "s"(p.row_blocks), "s"(p.rows), "s"(p.s_q),
+               "s"(p.h_q), "s"(p.heads), "s"(p.lse_base2), "s"(p.topk), "s"(p.num_rows), "s"(p.out),
+               "s"(p.lse), "s"(p.ws_o), "s"(p.ws_lse), "s"(p.max_logits), "s"(p.ws_max));
   const int total = p.num_parts * p.row_blocks;
   const int lg = logical_group(blockIdx.x, total);
   const int part = lg / p.row_blocks;

@@ -216,6 +216,12 @@ void mla_narrow(SplitKVParams p) {
   const int r = lane & 15;  // query row (QK B / C column), tile row (QK A row)
   const int g = lane >> 4;  // k-group of the MFMA operands
 
+  // the metadata pointer, the shape words and the output pointers are
+  // requested with the launch's part count, so the header reads below do not
+  // wait for further rounds of argument loads
+  asm volatile("" ::"s"(p.meta), "s"(p.num_parts), "s"(p.row_blocks), "s"(p.rows), "s"(p.s_q),
+               "s"(p.h_q), "s"(p.heads), "s"(p.lse_base2), "s"(p.topk), "s"(p.num_rows), "s"(p.out),
+               "s"(p.lse), "s"(p.ws_o), "s"(p.ws_lse), "s"(p.max_logits), "s"(p.ws_max));
   const int part = logical_group(blockIdx.x, p.num_parts);
   cint* meta = as_const(p.meta);
   // the grid covers p.num_parts parts, the device header says how many exist
