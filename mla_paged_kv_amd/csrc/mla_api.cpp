@@ -111,7 +111,6 @@ int launch_combine_stage(const int32_t* meta_dev, const mla_sched_info* info, in
   cp.max_logits = max_logits;
   cp.lse_base2 = lse_base2 ? 1 : 0;
   cp.out_f16 = f16 ? 1 : 0;
-  cp.off_num_splits = info->off_num_splits;
   cp.off_split_list = info->off_split_list;
   cp.num_split_units = info->num_split_units;
   cp.max_splits = info->max_splits;

@@ -68,15 +68,19 @@ __global__ __launch_bounds__(256) void mla_combine(CombineParams p) {
   // offsets and the split-unit count come from the host when it built the
   // metadata, else (negative offsets) from the device header, and the grid
   // then covers an upper bound of the split units
-  int off_sl = p.off_split_list, off_ns = p.off_num_splits;
+  int off_sl = p.off_split_list, nsu = p.num_split_units;
   if (off_sl < 0) {
-    if (k >= meta[3]) return;
-    off_ns = meta[13];
+    nsu = meta[3];
+    if (k >= nsu) return;
     off_sl = meta[14];
   }
+  // Split units own consecutive workspace slots, numbered in unit order, so
+  // unit k's split count is the next unit's first slot (or, for the last,
+  // the total slot count in header word 2) minus its own: read in the same
+  // round trip as the unit, not after it.
   const int u = meta[off_sl + 2 * k];
   const int slot0 = meta[off_sl + 2 * k + 1];
-  const int nsplit = meta[off_ns + u + 1] - meta[off_ns + u];
+  const int nsplit = meta[k + 1 < nsu ? off_sl + 2 * k + 3 : 2] - slot0;
   const float* lse_col = p.ws_lse + size_t(slot0) * p.rows + row;  // split s at s * rows
   const float* o_col = p.ws_o + (size_t(slot0) * p.rows + row) * kDV + 8 * lane;
   const size_t split_stride = size_t(p.rows) * kDV;

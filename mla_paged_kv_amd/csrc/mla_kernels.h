@@ -47,7 +47,7 @@ struct CombineParams {
   float* lse;
   float* max_logits;    // optional row maxima output
   int32_t lse_base2;
-  int32_t off_num_splits, off_split_list, num_split_units;
+  int32_t off_split_list, num_split_units;
   int32_t max_splits;  // most splits of any unit (picks the combine layout)
   int32_t out_f16;     // 1: out is fp16, 0: bf16
   int32_t rows, s_q, h_q, heads;
