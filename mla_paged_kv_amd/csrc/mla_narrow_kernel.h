@@ -232,9 +232,7 @@ void mla_narrow(SplitKVParams p) {
   const int h_parts = meta[0], h_segs = meta[12], h_status = meta[15];
   const int seg_begin = meta[kMetaHeaderInts + part];
   const int seg_end = meta[kMetaHeaderInts + part + 1];
-  // (the launch parameters the next steps need are requested with them)
-  asm volatile("" ::"s"(h_parts), "s"(h_segs), "s"(h_status), "s"(seg_begin), "s"(seg_end),
-               "s"(p.rows), "s"(p.s_q), "s"(p.h_q), "s"(p.heads), "s"(p.topk), "s"(p.num_rows));
+  asm volatile("" ::"s"(h_parts), "s"(h_segs), "s"(h_status), "s"(seg_begin), "s"(seg_end));
   const bool meta_bad = h_status == -1;
   if (part >= h_parts && !meta_bad) return;
   cint* segs = meta + h_segs;
@@ -380,7 +378,6 @@ void mla_narrow(SplitKVParams p) {
   float m_run = -__builtin_inff(), m_exact = -__builtin_inff(), l_part = 0.f;
   bool seg_first = true;
   int n_vis = 0;
-  size_t qrow = 0;
 
   auto load_q = [&](int u) __attribute__((always_inline)) {
     const uint16_t* qp = p.q + row_index(u, qr) * D_QK + 8 * g;
@@ -449,12 +446,14 @@ void mla_narrow(SplitKVParams p) {
   // LDS addresses of this lane's staged V (wavefront w's 16 rows at w x 16 KB)
   uint8_t* const vst = lds + wave * kVStage;
   // row writes: chunk 4 ks + g of row r -> (4 ks + g) ^ vsw(r); the XOR only
-  // touches the low 4 bits, so 4 bases (ks % 4) plus 256 (ks / 4) cover them
+  // touches the low 4 bits, so 4 per-lane bases (ks % 4) plus a compile-time
+  // 64 ks bytes cover every k-step
   int vw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) vw[j] = r * kVRow + 16 * (((4 * j + g) ^ vsw(r)) - 4 * j);
   // transpose reads of block cb: rows 4 g + rr (rr = (lane & 15) / 4), columns
-  // 16 cb + 4 c .. +3 (c = lane & 3) = chunk 2 cb + c / 2, byte 8 (c & 1)
+  // 16 cb + 4 c .. +3 (c = lane & 3) = chunk 2 cb + c / 2, byte 8 (c & 1);
+  // 8 per-lane bases (cb % 8) plus a compile-time 32 cb bytes
   int vr[8];
   {
     const int t = 4 * g + ((lane & 15) >> 2), c = lane & 3;
@@ -628,7 +627,6 @@ void mla_narrow(SplitKVParams p) {
   Tile nt{cs0, rec0[1], la_u, rec0[1] + 1 >= la_b1};
   Meta nmeta = fetch_meta(nt);
   load_q(nt.u);
-  qrow = row_index(nt.u, r);
   if constexpr (!SPARSE) n_vis = visible(nmeta.len);
   reset_state();
   // The metadata of the tile after is requested before a tile's row loads:
@@ -671,7 +669,6 @@ void mla_narrow(SplitKVParams p) {
       for (int e = t.s + 1; e < e_end; ++e) write_empty(seg_u(e), seg_slot(e));
       if (more) {
         const int un = sl_t[sn].u;
-        qrow = row_index(un, r);
         if constexpr (!SPARSE) n_vis = visible(as_const(p.seqlens)[un]);
         reset_state();
       }
@@ -694,7 +691,6 @@ void mla_narrow(SplitKVParams p) {
     }
     st = compute(std::integral_constant<int, 0>{});
   }
-  (void)qrow;
 #endif
 }
 
