@@ -208,6 +208,11 @@ void mla_narrow(SplitKVParams p) {
   static_assert(DEPTH >= 2 && DEPTH <= 4, "tiles in flight");
   static_assert(!FP8 || (D_QK == 576 && !F16), "FP8 rows: 512 e4m3 + 64 bf16 RoPE values, bf16 q");
   constexpr int NE = FP8 ? kDV / 32 : 1;  // FP8: k-steps held as e4m3 bytes (the value columns)
+  // FP8: the dot product over d_qk does not depend on the order of its terms,
+  // so k-step ks (< NE) of lane group g takes value columns 8 fp8_chunk(ks, g)
+  // .. +7 -- for K and Q alike -- and a lane's e4m3 bytes of two k-steps are
+  // 16 consecutive bytes, one load.  (bf16: chunk 4 ks + g.)
+  auto fp8_chunk = [](int ks, int gg) { return 8 * (ks >> 1) + 2 * gg + (ks & 1); };
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kXBytes];
   __shared__ float xstat[3][kWaves][kRows];  // per-wavefront row maxima, sums, exact maxima
 
@@ -365,10 +370,11 @@ void mla_narrow(SplitKVParams p) {
 
   // ---- registers ----
   // tile rows in flight (row r of the wavefront's 16): bf16 chunk 4 ks + g;
-  // FP8 rows: e4m3 bytes 32 ks + 8 g .. +7 of the value columns (kq), the
-  // row's 4 group scales (ksc) and the RoPE chunks 4 j + g (kr, j = ks - 16)
+  // FP8 rows: e4m3 bytes 64 j + 16 g .. +15 of the value columns (kq, the
+  // values of k-steps 2 j and 2 j + 1, see fp8_chunk), the row's 4 group
+  // scales (ksc) and the RoPE chunks 4 j + g (kr, j = ks - 16)
   bf16x8 kr[DEPTH][FP8 ? NK - NE : NK];
-  u32x2 kq[DEPTH][NE];
+  u32x4 kq[DEPTH][NE / 2 > 0 ? NE / 2 : 1];
   f32x4 ksc[DEPTH];
   Tile sl_t[DEPTH];      // the tile each slot holds
   bool sl_ok[DEPTH];     // the slot holds a tile of the stream
@@ -380,10 +386,11 @@ void mla_narrow(SplitKVParams p) {
   int n_vis = 0;
 
   auto load_q = [&](int u) __attribute__((always_inline)) {
-    const uint16_t* qp = p.q + row_index(u, qr) * D_QK + 8 * g;
+    const uint16_t* qrow = p.q + row_index(u, qr) * D_QK;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+      const int c = FP8 && ks < NE ? fp8_chunk(ks, g) : 4 * ks + g;
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 8 * c);
     }
   };
   auto reset_state = [&]() __attribute__((always_inline)) {
@@ -427,8 +434,8 @@ void mla_narrow(SplitKVParams p) {
       // the scales first: the first k-step's dequant then waits for two loads
       ksc[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + kDV, 0, 0));
 #pragma unroll
-      for (int ks = 0; ks < NE; ++ks)
-        kq[s][ks] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 32 * ks + 8 * g, 0, 0));
+      for (int j = 0; j < NE / 2; ++j)
+        kq[s][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * j + 16 * g, 0, 0));
 #pragma unroll
       for (int j = 0; j < NK - NE; ++j)
         kr[s][j] = __builtin_bit_cast(
@@ -451,6 +458,11 @@ void mla_narrow(SplitKVParams p) {
   int vw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) vw[j] = r * kVRow + 16 * (((4 * j + g) ^ vsw(r)) - 4 * j);
+  // FP8: chunk fp8_chunk(ks, g) = 16 (ks / 4) + fp8_chunk(ks % 4, g), so again
+  // 4 bases (ks % 4) plus a compile-time 256 (ks / 4) bytes
+  int vw8[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vw8[j] = r * kVRow + 16 * (fp8_chunk(j, g) ^ vsw(r));
   // transpose reads of block cb: rows 4 g + rr (rr = (lane & 15) / 4), columns
   // 16 cb + 4 c .. +3 (c = lane & 3) = chunk 2 cb + c / 2, byte 8 (c & 1);
   // 8 per-lane bases (cb % 8) plus a compile-time 32 cb bytes
@@ -529,12 +541,18 @@ void mla_narrow(SplitKVParams p) {
     f32x4 st;  // st[j]: token 16 w + 4 g + j, query row r
     if constexpr (FP8) {
       // dequantized k-step by k-step; the value columns go to the V stage
+      // at their own columns (chunk fp8_chunk(ks, g))
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        const bf16x8 a = ks < NE ? dequant8(kq[s][ks < NE ? ks : 0], ksc[s][(ks < NE ? ks : 0) / 4])
-                                 : kr[s][ks < NE ? 0 : ks - NE];
+        bf16x8 a;
+        if (ks < NE) {
+          const u32x4 w = kq[s][ks < NE ? ks >> 1 : 0];
+          a = dequant8((ks & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]}, ksc[s][(ks < NE ? ks : 0) / 4]);
+        } else {
+          a = kr[s][ks < NE ? 0 : ks - NE];
+        }
         mfma_qk<F16>(st, a, qf[ks], ks == 0);
-        if (ks < NV) *reinterpret_cast<bf16x8*>(vst + vw[ks & 3] + 64 * ks) = a;
+        if (ks < NV) *reinterpret_cast<bf16x8*>(vst + vw8[ks & 3] + 256 * (ks >> 2)) = a;
       }
       mfma_wait_result(st);
     } else {
