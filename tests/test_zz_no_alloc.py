@@ -40,12 +40,13 @@ def _same(a, b, what):
     assert np.array_equal(la, lb, equal_nan=True), f"{what}: LSE differs from mla_decode_paged"
 
 
-@pytest.mark.parametrize("device_meta", [False, True])
-def test_noalloc_matches_decode_paged_twice(device_meta):
+# the second call's units: 64 rows (the pair kernel) or 16 (the narrow kernel)
+@pytest.mark.parametrize("device_meta,small_h_q", [(False, 64), (True, 64), (False, 16), (True, 16)])
+def test_noalloc_matches_decode_paged_twice(device_meta, small_h_q):
     big = make_dense_case(71, B=8, s_q=2, h_q=128, causal=True,
                           seqlens=np.random.default_rng(71).integers(1, 4097, 8).tolist(),
                           table_width=64)
-    small = make_dense_case(72, B=3, s_q=1, h_q=64, seqlens=[1, 333, 700], table_width=16)
+    small = make_dense_case(72, B=3, s_q=1, h_q=small_h_q, seqlens=[1, 333, 700], table_width=16)
     runs = []
     for name, case in (("big", big), ("small", small)):
         d = to_device(case)
