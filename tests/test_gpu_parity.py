@@ -50,8 +50,9 @@ def test_tiny_workload():
 @pytest.mark.parametrize("s_q,causal,h_q,d_qk", [
     (1, False, 16, 576), (1, False, 128, 576), (2, True, 64, 576), (3, True, 16, 576),
     (1, False, 24, 576), (2, False, 8, 512), (1, False, 128, 512),
-    # units of 16 rows with causal masking (the narrow kernel)
-    (2, True, 8, 576),
+    # units of at most 16 rows (the narrow kernel): 16 rows with causal
+    # masking, 12 rows of 3 query tokens x 4 heads, a single row
+    (2, True, 8, 576), (3, True, 4, 576), (1, False, 1, 512),
     # units of 96, 80 and 160 rows: 128-row workgroups with wavefronts whose
     # 32 rows are all past the unit's, through segment changes (P = 1 walks
     # every request in one part)
