@@ -20,8 +20,8 @@ splits):
   "FP8 KV Cache"): both decode functions accept such a cache and dequantize
   the rows they read.
 * ``ref_sparse_prefill`` -- sparse MLA prefill (same README, "Sparse MLA
-  Prefill": out, max_logits and a base-2 LSE, in the order of its equivalent
-  PyTorch code).
+  Prefill": out, max_logits and a base-2 LSE, written from the softmax
+  definition those outputs have).
 * ``ref_schedule``       -- the reference tile scheduler.  The pages give only
   its purpose (metadata from sequence lengths and the head configuration that
   spreads variable-length work over compute units); the algorithm is this
