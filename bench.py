@@ -513,8 +513,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
-                                   "design note, not an implemented path", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "bench.py runs on one GPU only: sharding the decode over "
+                                   "several GPUs is described, not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch

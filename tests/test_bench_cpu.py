@@ -120,3 +120,15 @@ def test_counter_ingestion_takes_the_narrow_kernel(tmp_path, monkeypatch):
     _write_counter_csv(w, "WRITE_SIZE", [(neg, "WRITE_SIZE", probe_kib), (narrow, "WRITE_SIZE", 8.0)])
     out = bench.ingest_counters(5, str(f), str(w), "cmd")
     assert out["traffic_bytes_per_launch"] == (64 + 8) * 1024
+
+
+def test_more_than_one_gpu_is_refused():
+    """--gpus N with N > 1 exits with status 2 and says why, before any GPU work."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU only" in msg["error"]
